@@ -1,0 +1,190 @@
+/*
+ * strata_window.h - C ABI of the batched verify-window MoE layer for gfx950 (MI355X).
+ *
+ * What the layer computes (Strata, docs/BATCHING.md "Several requests at once (batch
+ * slots)", opening paragraph): a verify window carries one row per active conversation
+ * slot (two rows per slot when each slot also verifies one MTP proposal, same page,
+ * the --batch-mtp paragraph), at most eight rows (same page, option table and the
+ * paragraph after it; PR #1636 "What changed": the hand-off bound is kVerifyMaxT rows).
+ * The router, the shared expert, every routed expert used by any row of the window and
+ * the output head are read once per window for all rows that use them. A row's
+ * arithmetic does not depend on which other rows share the window (same page,
+ * "Exactness"), so every kernel behind this ABI computes a row the same way whether it
+ * is alone or grouped with others.
+ *
+ * Conventions for every entry point
+ *   - Stateless: the library keeps no state between calls.
+ *   - Every pointer argument except `stream` and the descriptor structs themselves is a
+ *     DEVICE pointer owned by the caller, valid until the work enqueued on `stream` has
+ *     finished. The descriptor structs (strata_qmat, strata_route_out) are read on the
+ *     host during the call only.
+ *   - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the default
+ *     stream). No call allocates, frees or synchronises, so calls may be captured into a
+ *     HIP graph.
+ *   - Device pointers must be 16-byte aligned; `ws` must be 256-byte aligned.
+ *   - Return value: 0 on success, or a negative status (below). On error nothing has
+ *     been enqueued, except for STRATA_EHIP, where a launch failed;
+ *     strata_window_last_error() then describes the failure (thread-local string).
+ *   - Workspace `ws`: at least strata_window_workspace(...) bytes. Its first
+ *     STRATA_WS_COUNTER_BYTES bytes hold completion counters that must be zero before
+ *     the first call that uses the buffer (e.g. one hipMemset at allocation); every call
+ *     returns them to zero when its work completes. Two calls whose work may overlap in
+ *     time must not share a workspace.
+ *
+ * Limits: 1 <= rows <= 8; 1 <= top_k <= 8; top_k <= n_experts <= 256.
+ */
+#ifndef STRATA_WINDOW_H
+#define STRATA_WINDOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STRATA_WINDOW_ABI_VERSION 1
+
+enum { STRATA_OK = 0, STRATA_EINVAL = -1, STRATA_EUNSUPPORTED = -2, STRATA_EHIP = -3 };
+enum { STRATA_F32 = 0, STRATA_BF16 = 1 };       /* activation dtypes                */
+enum { STRATA_ROUTE_RENORM = 1 };                /* route flag: divide top-k weights
+                                                    by their sum                     */
+enum { STRATA_MAX_ROWS = 8, STRATA_MAX_TOPK = 8, STRATA_MAX_EXPERTS = 256 };
+#define STRATA_WS_COUNTER_BYTES 4096
+
+/*
+ * strata_qmat - one block-quantized matrix W[rows][cols] (rows = outputs, cols = inputs),
+ * or n_mat of them stacked (the routed experts of one projection).
+ *
+ * Dequantisation, blocks of 32 consecutive inputs k of one row n, block b = k / 32:
+ *   bits 4 or 2 (affine):   W[n][k] = scale[n][b] * q + min[n][b],  q unsigned in [0, 2^bits)
+ *   bits 8 (symmetric):     W[n][k] = scale[n][b] * q,              q two's-complement int8
+ * scale and min are IEEE binary16.
+ *
+ * Code layout (per matrix). G = 512 / bits inputs form a k-group (4-bit: 128, 2-bit: 256,
+ * 8-bit: 64); rows form tiles of 16. Each (row tile t, k-group g) owns one 1024-byte
+ * chunk, chunks ordered t-major: chunk index c = t * (cols / G) + g. Inside a chunk,
+ * 64 lanes of 16 bytes; lane L = 16 * j + (n % 16) holds, for row n, the inputs
+ * k = G*g + 32*beta + 8*j + i  (beta = block within the group, i in [0,8)),
+ * the code of (beta, i) occupying bits [bits*(8*beta + i), bits*(8*beta + i) + bits) of the
+ * lane's 128-bit little-endian word. So for weight (n, k):
+ *     t = n/16, g = k/G, beta = (k%G)/32, j = (k%32)/8, i = k%8, L = 16*j + n%16
+ *     bit = bits*(8*beta + i)
+ *     byte offset = (c*64 + L)*16 + bit/8,  code = (byte >> (bit%8)) & (2^bits - 1)
+ *
+ * Meta layout (per matrix), the same chunk order: chunk c holds 16 rows x (G/32) blocks,
+ * row-major: element index = (c*16 + n%16) * (G/32) + beta.
+ *     bits 4/2: uint32 per block = scale | (min << 16)      (binary16 bit patterns)
+ *     bits 8:   uint16 per block = scale
+ *
+ * Requirements: rows % 16 == 0, cols % G == 0, bits in {2, 4, 8}.
+ * Stacked matrices: matrix m starts at codes + m*mat_stride_codes bytes and at
+ * meta element m*mat_stride_meta (strides 0 when n_mat == 1); strides must keep
+ * 16-byte alignment.
+ */
+typedef struct {
+  const void* codes;
+  const void* meta;
+  int32_t rows, cols, bits;
+  int32_t n_mat;
+  int64_t mat_stride_codes;   /* bytes    */
+  int64_t mat_stride_meta;    /* elements */
+} strata_qmat;
+
+/*
+ * strata_route_out - routing of one window (written by strata_window_route, read by
+ * strata_window_moe). All device pointers, sized by the caller (R = rows, k = top_k,
+ * E = n_experts, A = min(E, R*k) + 1):
+ *   topk_idx [R*k] int32  row r's experts, by descending logit, ties to the lower index
+ *   topk_w   [R*k] float  softmax probability of that expert (renormalised over the
+ *                         row's k experts with STRATA_ROUTE_RENORM)
+ *   n_active [1]   int32  number of active experts, shared expert included
+ *   active   [A]   int32  active expert ids ascending; the shared expert (id E) last
+ *   offsets  [A+1] int32  entries of active[a] are offsets[a] .. offsets[a+1]-1
+ *   entry_row[R*k+R] int32  row of each entry, ascending within an expert
+ *   entry_w  [R*k+R] float  routing weight of each entry (1 for the shared expert)
+ *   row_mask [E+1] uint8  bit r set when row r uses that expert (entry E: all rows)
+ * Entries past n_active / offsets[n_active] are left untouched.
+ */
+typedef struct {
+  int32_t* topk_idx;
+  float*   topk_w;
+  int32_t* n_active;
+  int32_t* active;
+  int32_t* offsets;
+  int32_t* entry_row;
+  float*   entry_w;
+  uint8_t* row_mask;
+} strata_route_out;
+
+/*
+ * strata_window_route - router GEMV, softmax, top-k and per-expert row grouping for one
+ * window (Strata docs/BATCHING.md, opening paragraph: every routed expert the rows share
+ * is read once per window; the grouping lists the rows of each expert).
+ *   x        [rows][hidden], x_dtype STRATA_F32 or STRATA_BF16, row-major
+ *   gate_w   [n_experts][hidden] float, row-major
+ *   logit_bias [n_experts] float or NULL: added to each row's logits before softmax/top-k
+ *   logit[r][e] = sum_h gate_w[e][h] * x[r][h] + bias[e], accumulated in double from
+ *   exact products; p = softmax over all experts; the top_k largest logits are selected.
+ *   flags: 0 or STRATA_ROUTE_RENORM.
+ * Errors: STRATA_EINVAL for a null or misaligned pointer, a bad dtype or flag, sizes
+ * outside the limits, hidden % 64 != 0, or a workspace smaller than
+ * strata_window_workspace(0, ...).
+ */
+int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int hidden,
+                        const float* gate_w, const float* logit_bias, int n_experts,
+                        int top_k, int flags, const strata_route_out* out,
+                        void* ws, size_t ws_bytes);
+
+/*
+ * strata_window_moe - the experts of one window: for every active expert and each of its
+ * rows, h = silu(W_gate x) * (W_up x) with silu(z) = z / (1 + exp(-z)), y = W_down h;
+ * then for each row r
+ *   out[r] = sum over r's entries (ascending expert id) of entry_w * y  +  y_shared
+ *            (+ residual[r] when residual != NULL)
+ * (Strata docs/BATCHING.md, opening paragraph: the shared expert and the routed experts
+ * are read once per window for all rows that use them.)
+ *   x        [rows][hidden], x_dtype; residual NULL or [rows][hidden] of x_dtype
+ *   gate, up: n_mat = n_experts matrices [ffn][hidden]; down: [hidden][ffn]
+ *   sh_gate, sh_up, sh_down: the shared expert, n_mat = 1, same shapes and bits
+ *   route    the output of strata_window_route for this window (same rows, experts, k)
+ *   out      [rows][hidden] float
+ *   x_next_bf16 NULL or [rows][hidden] bf16: round-to-nearest-even of out
+ * Intermediates stay in float. Bits 4 or 2 (all six matrices alike).
+ * Errors: STRATA_EINVAL as for route, or mismatched matrix shapes/bits, or a workspace
+ * smaller than strata_window_workspace(1, ...); STRATA_EUNSUPPORTED for bits 8 here.
+ */
+int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hidden,
+                      int ffn, const strata_qmat* gate, const strata_qmat* up,
+                      const strata_qmat* down, const strata_qmat* sh_gate,
+                      const strata_qmat* sh_up, const strata_qmat* sh_down,
+                      const strata_route_out* route, int n_experts, int top_k,
+                      const void* residual, float* out, uint16_t* x_next_bf16,
+                      void* ws, size_t ws_bytes);
+
+/*
+ * strata_window_head - the output head of the window (Strata docs/BATCHING.md, opening
+ * paragraph: the head is read once per window; docs/MULTI_GPU.md "What each card
+ * holds": the last card runs it): logits[r][v] = sum_h W[v][h] * x[r][h] over an 8-bit
+ * block-quantized W [vocab][hidden], then argmax[r] = the lowest v of the largest logit.
+ *   logits NULL or [rows][vocab] float; argmax [rows] int32.
+ * Errors: STRATA_EINVAL as above (head bits must be 8, rows == vocab, cols == hidden).
+ */
+int strata_window_head(void* stream, const void* x, int x_dtype, int rows, int hidden,
+                       const strata_qmat* head, int vocab, float* logits,
+                       int32_t* argmax, void* ws, size_t ws_bytes);
+
+/* Workspace bytes for which = 0 (route), 1 (moe), 2 (head); 0 for invalid arguments. */
+size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts,
+                               int top_k, int vocab);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* strata_window_last_error(void);
+
+/* STRATA_WINDOW_ABI_VERSION of the built library. */
+int strata_window_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STRATA_WINDOW_H */

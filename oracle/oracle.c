@@ -1,0 +1,324 @@
+/*
+ * oracle.c - TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, scalar CPU reference of the batched verify-window MoE layer, computed
+ * in double precision. Only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark load it; the product path never does. It shares no code, header, table or
+ * helper with the HIP library: it decodes the documented byte layout itself and follows
+ * the per-row definition of the layer.
+ *
+ * Source of the method (Strata docs):
+ *   - docs/BATCHING.md "Several requests at once (batch slots)", opening paragraph: a
+ *     window carries one row per conversation slot and reads the router, the shared
+ *     expert, the head and every routed expert the rows use once for all of them.
+ *   - same page, "Exactness": a batch row's arithmetic is the one of a single-token
+ *     window. So the reference computes each row alone, from its definition; grouping
+ *     is computed separately (oracle_group) only to check the grouping the GPU builds.
+ * Where the pages leave a step open, the readings taken are:
+ *   affine dequant w = scale*q + min (q unsigned), symmetric 8-bit w = scale*q;
+ *   softmax over all experts, top-k selected on logits, ties to the lower expert index;
+ *   top-k weights = softmax probabilities (optionally renormalised over the k chosen);
+ *   shared expert ungated with weight 1; SwiGLU h = silu(gate)*up, silu(z) = z/(1+e^-z);
+ *   residual and next-layer input x_next = bf16_round_nearest_even(x + moe(x)).
+ *
+ * Every floating-point operation is IEEE double, without fused multiply-add
+ * (build with -ffp-contract=off). Inputs in bf16, binary16 and float convert to double
+ * exactly; every product of a weight and an activation is exact in double.
+ *
+ * Parallelism: OpenMP only across independent (row, expert) evaluations; their results
+ * are combined serially in a fixed order, so the output does not depend on the thread
+ * count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+
+/* One quantized matrix (or n_mat stacked ones), as the layout documentation states. */
+typedef struct {
+  const uint8_t* codes;
+  const void* meta;
+  int32_t rows, cols, bits;
+  int32_t n_mat;
+  int64_t mat_stride_codes; /* bytes */
+  int64_t mat_stride_meta;  /* meta elements */
+} oracle_qmat;
+
+/* ------------------------------------------------------------------ number formats */
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);               /* subnormal: m * 2^-24 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25);   /* (1 + m/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest bfloat16 (8 significant bits), ties to even. */
+uint16_t oracle_double_to_bf16(double v) {
+  if (isnan(v)) return 0x7FC0;
+  if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+  int e;
+  frexp(v, &e);                      /* |v| = f * 2^e, 0.5 <= f < 1 */
+  int qexp = e - 8;                  /* quantum of an 8-bit significand */
+  if (qexp < -133) qexp = -133;      /* subnormal bf16 quantum 2^-133 */
+  double r = rint(ldexp(v, -qexp));  /* default rounding mode: nearest, ties to even */
+  double rv = ldexp(r, qexp);
+  if (fabs(rv) >= ldexp(1.0, 128)) return signbit(v) ? 0xFF80 : 0x7F80;  /* overflow */
+  float f = (float)rv;               /* exact: rv has <= 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+static double act(const void* x, int dtype, long idx) {
+  if (dtype == OR_F32) return (double)((const float*)x)[idx];
+  return oracle_bf16_to_double(((const uint16_t*)x)[idx]);
+}
+
+/* ---------------------------------------------------------------- quantized layout */
+
+static int group_width(int bits) { return 512 / bits; } /* inputs per k-group */
+
+/* Code of weight (n, k) of matrix `mat`, decoded from the documented chunk layout. */
+int oracle_code(const oracle_qmat* q, int mat, int n, int k) {
+  const int bits = q->bits, G = group_width(bits);
+  const long t = n / 16, g = k / G, beta = (k % G) / 32, j = (k % 32) / 8, i = k % 8;
+  const long lane = 16 * j + n % 16;
+  const long chunk = t * (q->cols / G) + g;
+  const long bit = (long)bits * (8 * beta + i);
+  const uint8_t* base = q->codes + (long)mat * q->mat_stride_codes;
+  const uint8_t byte = base[(chunk * 64 + lane) * 16 + bit / 8];
+  int code = (byte >> (bit % 8)) & ((1 << bits) - 1);
+  if (bits == 8 && code >= 128) code -= 256; /* two's complement */
+  return code;
+}
+
+/* Scale and min of block b (= k / 32) of row n; min is 0 for 8-bit matrices. */
+void oracle_block_meta(const oracle_qmat* q, int mat, int n, int b, double* scale,
+                       double* min) {
+  const int G = group_width(q->bits), bpg = G / 32;
+  const long t = n / 16, g = b / bpg, beta = b % bpg;
+  const long chunk = t * (q->cols / G) + g;
+  const long idx = (long)mat * q->mat_stride_meta + (chunk * 16 + n % 16) * bpg + beta;
+  if (q->bits == 8) {
+    *scale = oracle_f16_to_double(((const uint16_t*)q->meta)[idx]);
+    *min = 0.0;
+  } else {
+    const uint32_t m = ((const uint32_t*)q->meta)[idx];
+    *scale = oracle_f16_to_double((uint16_t)(m & 0xFFFF));
+    *min = oracle_f16_to_double((uint16_t)(m >> 16));
+  }
+}
+
+/* Dequantized weight W[n][k] of matrix `mat`. */
+double oracle_weight(const oracle_qmat* q, int mat, int n, int k) {
+  double s, m;
+  oracle_block_meta(q, mat, n, k / 32, &s, &m);
+  return s * (double)oracle_code(q, mat, n, k) + m;
+}
+
+/* Whole matrix `mat` dequantized into out[rows][cols] (used by the tests' pins). */
+void oracle_dequant(const oracle_qmat* q, int mat, double* out) {
+  for (int n = 0; n < q->rows; n++)
+    for (int k = 0; k < q->cols; k++) out[(long)n * q->cols + k] = oracle_weight(q, mat, n, k);
+}
+
+/* ------------------------------------------------------------------------ routing */
+
+/*
+ * Router of a window: logits, softmax probabilities, top-k experts and their weights.
+ *   logits[r][e] = sum_h G[e][h] * x[r][h]  (h ascending)  + bias[e]
+ *   probs[r][e]  = exp(logit - max) / sum_e' exp(logit' - max)
+ *   topk: the k largest logits, descending; equal logits -> lower expert index first
+ *   topk_w = probs of the chosen experts, divided by their sum when renorm != 0
+ */
+void oracle_route(const void* x, int x_dtype, int R, int H, const float* G,
+                  const float* bias, int E, int K, int renorm, double* logits,
+                  double* probs, int32_t* topk_idx, double* topk_w) {
+  for (int r = 0; r < R; r++) {
+    double* l = logits + (long)r * E;
+    for (int e = 0; e < E; e++) {
+      double s = 0.0;
+      for (int h = 0; h < H; h++) s += (double)G[(long)e * H + h] * act(x, x_dtype, (long)r * H + h);
+      l[e] = s + (bias ? (double)bias[e] : 0.0);
+    }
+    double mx = l[0];
+    for (int e = 1; e < E; e++)
+      if (l[e] > mx) mx = l[e];
+    double z = 0.0;
+    for (int e = 0; e < E; e++) z += exp(l[e] - mx);
+    for (int e = 0; e < E; e++) probs[(long)r * E + e] = exp(l[e] - mx) / z;
+
+    /* selection: repeatedly take the best expert not yet taken */
+    char taken[1024];
+    memset(taken, 0, sizeof taken);
+    for (int j = 0; j < K; j++) {
+      int best = -1;
+      for (int e = 0; e < E; e++) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e; /* strict '>' keeps the lower index */
+      }
+      taken[best] = 1;
+      topk_idx[r * K + j] = best;
+      topk_w[r * K + j] = probs[(long)r * E + best];
+    }
+    if (renorm) {
+      double s = 0.0;
+      for (int j = 0; j < K; j++) s += topk_w[r * K + j];
+      for (int j = 0; j < K; j++) topk_w[r * K + j] /= s;
+    }
+  }
+}
+
+/*
+ * Per-expert row lists of the window, from the top-k choice: experts ascending, each
+ * with its rows ascending; the shared expert (id E) last with every row and weight 1.
+ * Returns the number of active experts.
+ */
+int oracle_group(int R, int E, int K, const int32_t* topk_idx, const double* topk_w,
+                 int32_t* active, int32_t* offsets, int32_t* entry_row,
+                 double* entry_w, uint8_t* row_mask) {
+  int n = 0, pos = 0;
+  for (int e = 0; e <= E; e++) {
+    unsigned mask = 0;
+    for (int r = 0; r < R; r++) {
+      if (e == E) { mask |= 1u << r; continue; }
+      for (int j = 0; j < K; j++)
+        if (topk_idx[r * K + j] == e) mask |= 1u << r;
+    }
+    row_mask[e] = (uint8_t)mask;
+    if (!mask) continue;
+    active[n] = e;
+    offsets[n] = pos;
+    for (int r = 0; r < R; r++) {
+      if (!(mask >> r & 1)) continue;
+      double w = 1.0;
+      if (e < E)
+        for (int j = 0; j < K; j++)
+          if (topk_idx[r * K + j] == e) w = topk_w[r * K + j];
+      entry_row[pos] = r;
+      entry_w[pos] = w;
+      pos++;
+    }
+    n++;
+  }
+  offsets[n] = pos;
+  return n;
+}
+
+/* ------------------------------------------------------------------------ experts */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * One expert on one row: h[f] = silu(sum_k Wg[f][k] x[k]) * (sum_k Wu[f][k] x[k]),
+ * y[n] = sum_f Wd[n][f] h[f]; every sum with its index ascending.
+ */
+void oracle_expert(const oracle_qmat* gate, const oracle_qmat* up, const oracle_qmat* down,
+                   int mat, const double* xr, int H, int F, double* y) {
+  double* h = (double*)malloc(sizeof(double) * F);
+  for (int f = 0; f < F; f++) {
+    double g = 0.0, u = 0.0;
+    for (int k = 0; k < H; k++) g += oracle_weight(gate, mat, f, k) * xr[k];
+    for (int k = 0; k < H; k++) u += oracle_weight(up, mat, f, k) * xr[k];
+    h[f] = silu(g) * u;
+  }
+  for (int n = 0; n < H; n++) {
+    double s = 0.0;
+    for (int f = 0; f < F; f++) s += oracle_weight(down, mat, n, f) * h[f];
+    y[n] = s;
+  }
+  free(h);
+}
+
+/*
+ * The experts of a window, row by row from the definition:
+ *   out[r] = sum_j topk_w[r][j] * FFN_{topk_idx[r][j]}(x_r) + FFN_shared(x_r)
+ *            (+ residual[r] when residual != NULL)
+ * summed in the order j = 0..K-1, shared last, then the residual.
+ * x_next (may be NULL) = bf16 round-to-nearest-even of out.
+ */
+void oracle_moe(const void* x, int x_dtype, int R, int H, int F, const oracle_qmat* gate,
+                const oracle_qmat* up, const oracle_qmat* down, const oracle_qmat* sh_gate,
+                const oracle_qmat* sh_up, const oracle_qmat* sh_down, int K,
+                const int32_t* topk_idx, const double* topk_w, const void* residual,
+                double* out, uint16_t* x_next) {
+  const int per_row = K + 1;
+  double* xd = (double*)malloc(sizeof(double) * R * H);
+  double* y = (double*)malloc(sizeof(double) * (long)R * per_row * H);
+  for (long i = 0; i < (long)R * H; i++) xd[i] = act(x, x_dtype, i);
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < R * per_row; t++) {
+    const int r = t / per_row, j = t % per_row;
+    double* yt = y + (long)t * H;
+    if (j < K)
+      oracle_expert(gate, up, down, topk_idx[r * K + j], xd + (long)r * H, H, F, yt);
+    else
+      oracle_expert(sh_gate, sh_up, sh_down, 0, xd + (long)r * H, H, F, yt);
+  }
+
+  for (int r = 0; r < R; r++)
+    for (int n = 0; n < H; n++) {
+      double s = 0.0;
+      for (int j = 0; j < K; j++) s += topk_w[r * K + j] * y[((long)r * per_row + j) * H + n];
+      s += y[((long)r * per_row + K) * H + n];
+      if (residual) s += act(residual, x_dtype, (long)r * H + n);
+      out[(long)r * H + n] = s;
+      if (x_next) x_next[(long)r * H + n] = oracle_double_to_bf16(s);
+    }
+  free(y);
+  free(xd);
+}
+
+/* --------------------------------------------------------------------------- head */
+
+/*
+ * Output head: logits[r][v] = sum_h W[v][h] x[r][h] (h ascending) for the rows' vocab
+ * entries v in [v0, v1); argmax over that range, the lowest v on ties. logits is
+ * [R][v1 - v0]. (A sub-range lets the tests sample a large vocabulary.)
+ */
+void oracle_head(const void* x, int x_dtype, int R, int H, const oracle_qmat* head, int v0,
+                 int v1, double* logits, int32_t* argmax) {
+  const int nv = v1 - v0;
+#pragma omp parallel for schedule(static)
+  for (int v = v0; v < v1; v++)
+    for (int r = 0; r < R; r++) {
+      double s = 0.0;
+      for (int h = 0; h < H; h++) s += oracle_weight(head, 0, v, h) * act(x, x_dtype, (long)r * H + h);
+      logits[(long)r * nv + (v - v0)] = s;
+    }
+  for (int r = 0; r < R; r++) {
+    int best = 0;
+    for (int v = 1; v < nv; v++)
+      if (logits[(long)r * nv + v] > logits[(long)r * nv + best]) best = v;
+    argmax[r] = v0 + best;
+  }
+}
+
+/* Threads OpenMP would use for the parallel loops above (1 without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
