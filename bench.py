@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Throughput of the batched verify-window MoE layer on one MI355X.
+
+A step is one verify window through the whole layer: router GEMV + softmax + top-k +
+per-expert row grouping (strata_window_route), then fused dequant gate/up + SwiGLU, down
+and the weighted combine with the shared expert (strata_window_moe). The default
+workload is the 8-row window (4 slots x token + MTP proposal, Zipf(1.1) router prior,
+correlated pairs) of a 2048-hidden / 768-ffn / 128-expert top-8 layer with 4-bit block
+quantization. --config 3 runs the 24-layer stack with the 8-bit head instead (a step is
+then one window through all 24 layers and the head).
+
+Timing: K steps are captured into one HIP graph (inputs resident in HBM) and replayed
+once between two synchronisations; steps cycle through L independent layer instances so
+that the 256 MB Infinity Cache cannot serve a layer's weights from a previous visit.
+The achieved bandwidth counts the unique weight bytes each window reads (router +
+(distinct routed experts + 1 shared) x expert bytes), from the window's own routing.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+METRIC = "verify-window MoE layer rows/s and achieved HBM GB/s (% of peak), 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2048)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    p.add_argument("--rows", type=int, default=None, help="window rows (config 4 sweep)")
+    p.add_argument("--layers", type=int, default=16, help="layer instances to cycle through")
+    p.add_argument("--windows", type=int, default=256, help="distinct activation windows")
+    p.add_argument("--prof-steps", type=int, default=512, help="eager steps timed per kernel")
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget (0: skip)")
+    return p.parse_args()
+
+
+def bpw(bits):
+    """Bytes per weight including the per-block metadata (4 bytes per 32 weights)."""
+    return bits / 8.0 + 4.0 / 32.0
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = ["verify_window_expert_amd/csrc/moe.hip", "verify_window_expert_amd/csrc/common.h"]
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, when it was taken from the
+    current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256_16") != source_sha(KERNEL_SOURCES):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Steps:
+    """Device state of K steps: layers, windows, per-step routing outputs, workspaces."""
+
+    def __init__(self, cfg, n_layers, n_windows, steps, sw, torch, synth, DevLayer, to_dev_x):
+        self.cfg, self.sw, self.torch = cfg, sw, torch
+        R, H, E, k = cfg.rows, cfg.hidden, cfg.experts, cfg.top_k
+        t0 = time.time()
+        self.layers = []
+        self.host_layer0 = None
+        for l in range(n_layers):
+            L = synth.make_layer(cfg, l)
+            self.layers.append(DevLayer(L, cfg))
+            if l == 0:
+                self.host_layer0 = L
+            log(f"[bench] layer {l + 1}/{n_layers} resident ({time.time() - t0:.1f}s)")
+        self.xs = [to_dev_x(synth.make_window(cfg, w, rows=R)) for w in range(n_windows)]
+        # per-step routing outputs: views into padded device arrays (16-byte aligned slices)
+        A = min(E, R * k) + 1
+        ent = R * k + R
+        pad = lambda n: (n + 63) // 64 * 64
+        i32, f32 = torch.int32, torch.float32
+        dev = "cuda"
+        self.big = dict(topk_idx=torch.empty(steps, pad(R * k), dtype=i32, device=dev),
+                        topk_w=torch.empty(steps, pad(R * k), dtype=f32, device=dev),
+                        n_active=torch.zeros(steps, 64, dtype=i32, device=dev),
+                        active=torch.empty(steps, pad(A), dtype=i32, device=dev),
+                        offsets=torch.empty(steps, pad(A + 1), dtype=i32, device=dev),
+                        entry_row=torch.empty(steps, pad(ent), dtype=i32, device=dev),
+                        entry_w=torch.empty(steps, pad(ent), dtype=f32, device=dev),
+                        row_mask=torch.empty(steps, pad(E + 1), dtype=torch.uint8, device=dev))
+        self.routes = []
+        for i in range(steps):
+            ro = sw.RouteOut.__new__(sw.RouteOut)
+            ro.rows, ro.n_experts, ro.top_k = R, E, k
+            for name, t in self.big.items():
+                setattr(ro, name, t[i])
+            self.routes.append(ro)
+        self.ws_r = sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E))
+        self.ws_m = sw.workspace(sw.workspace_bytes(1, R, H, cfg.ffn, E, k))
+        self.out = torch.empty(R, H, dtype=torch.float32, device=dev)
+
+    def step(self, i, prof_route=None, prof_moe=None):
+        cfg, sw = self.cfg, self.sw
+        dl = self.layers[i % len(self.layers)]
+        x = self.xs[i % len(self.xs)]
+        ro = sw.strata_window_route(x, dl.gate_w, dl.bias, cfg.top_k, out=self.routes[i], ws=self.ws_r,
+                                    prof=prof_route)
+        sw.strata_window_moe(x, dl.gate, dl.up, dl.down, *dl.sh, ro, out=self.out, ws=self.ws_m, prof=prof_moe)
+
+    def distinct_experts(self, steps):
+        return (self.big["n_active"][:steps, 0] - 1).cpu().numpy()
+
+
+def device_layer_types(torch, sw):
+    """Upload helpers: a layer's weights and a window's activations on the device."""
+    import numpy as np
+
+    def to_dev_x(x):
+        if x.dtype == np.float32:
+            return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    class DevLayer:
+        def __init__(self, layer, cfg):
+            H, F, b = cfg.hidden, cfg.ffn, cfg.bits
+            self.gate_w = torch.from_numpy(layer.gate_w).cuda()
+            self.bias = None if layer.bias is None else torch.from_numpy(layer.bias).cuda()
+            up = lambda m, r, c: sw.upload_qmat(m[0], m[1], r, c, b)
+            self.gate, self.up, self.down = up(layer.gate, F, H), up(layer.up, F, H), up(layer.down, H, F)
+            self.sh = (up(layer.sh_gate, F, H), up(layer.sh_up, F, H), up(layer.sh_down, H, F))
+
+    return DevLayer, to_dev_x
+
+
+def events(torch, n):
+    """n timing events, created (recorded once) so their handles exist."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def cpu_baseline(cfg, host_layer, seconds):
+    """The CPU oracle, as it stands, on windows of the same workload until `seconds` pass."""
+    import oracle
+    import synth
+    oracle.build(force=False)
+    H, F, E, b = cfg.hidden, cfg.ffn, cfg.experts, cfg.bits
+    q = lambda m, n, r, c: oracle.qmat(m[0], m[1], r, c, b, n)
+    L = host_layer
+    mats = (q(L.gate, E, F, H), q(L.up, E, F, H), q(L.down, E, H, F),
+            q(L.sh_gate, 1, F, H), q(L.sh_up, 1, F, H), q(L.sh_down, 1, H, F))
+    n, t0 = 0, time.time()
+    while True:
+        x = synth.make_window(cfg, n, rows=cfg.rows)
+        _, _, idx, w = oracle.route(x, L.gate_w, L.bias, cfg.top_k)
+        oracle.group(idx, w, E)
+        oracle.moe(x, *mats, idx, w)
+        n += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    return {"value": round(cfg.rows * n / dt, 3), "unit": "rows/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} windows of this workload (layer instance 0, windows 0..{n - 1}): route, grouping and "
+                      f"experts, {dt:.1f} s wall clock, OpenMP threads = {oracle.threads()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    import synth
+    import verify_window_expert_amd as sw
+    sw.library()   # raises if the HIP library is not built
+    DevLayer, to_dev_x = device_layer_types(torch, sw)
+
+    if args.config == 3:
+        return bench_stack(args, torch, synth, sw, DevLayer, to_dev_x)
+    cfg = synth.config(args.config, **({"rows": args.rows} if args.rows else {}))
+    K, W = args.steps, args.warmup
+    st = Steps(cfg, args.layers, args.windows, max(K, args.prof_steps), sw, torch, synth, DevLayer, to_dev_x)
+
+    for i in range(W):
+        st.step(i)
+    torch.cuda.synchronize()
+
+    # ---- per-kernel durations: eager steps, events recorded by the dispatches themselves
+    P = min(args.prof_steps, K)
+    evs = events(torch, 6 * P)
+    for i in range(P):
+        e = evs[6 * i: 6 * i + 6]
+        st.step(i, prof_route=[e[0].cuda_event, e[1].cuda_event],
+                prof_moe=[e[2].cuda_event, e[3].cuda_event, e[4].cuda_event, e[5].cuda_event])
+    torch.cuda.synchronize()
+    d_route = [evs[6 * i].elapsed_time(evs[6 * i + 1]) for i in range(P)]
+    d_gu = [evs[6 * i + 2].elapsed_time(evs[6 * i + 3]) for i in range(P)]
+    d_dn = [evs[6 * i + 4].elapsed_time(evs[6 * i + 5]) for i in range(P)]
+    U_prof = st.distinct_experts(P)
+
+    # ---- the timed region: one graph of K steps
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(K):
+                st.step(i)
+    torch.cuda.synchronize()
+    g.replay()                      # warm replay
+    torch.cuda.synchronize()
+    # replay() runs on the current stream: the events go there too
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    U = st.distinct_experts(K)
+
+    H, F, E, R = cfg.hidden, cfg.ffn, cfg.experts, cfg.rows
+    b_x = 3 * F * H * bpw(cfg.bits)
+    b_r = 4 * E * H + (4 * E if cfg.zipf else 0)
+    bytes_total = float(sum(b_r + (u + 1) * b_x for u in U))
+    gbs = bytes_total / (ms_total * 1e-3) / 1e9
+    rows_s = R * K / (ms_total * 1e-3)
+
+    # dominant kernel: gate/up (two thirds of the window's bytes)
+    gu_bytes = [(u + 1) * 2 * F * H * bpw(cfg.bits) for u in U_prof]
+    gu_gbs = sum(gu_bytes) / (sum(d_gu) * 1e-3) / 1e9
+    traffic = counter_traffic("k_gateup", f"config{cfg.cid}")
+    roof = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": "k_gateup (fused 4-bit dequant gate/up matvec + SwiGLU)" if cfg.bits == 4 else
+                      "k_gateup (fused 2-bit dequant gate/up matvec + SwiGLU)",
+            "avg_launch_us": round(1e3 * sum(d_gu) / P, 3),
+            "algorithmic_bytes_per_launch": round(sum(gu_bytes) / P)}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget)")
+        cpu = cpu_baseline(cfg, st.host_layer0, args.cpu_seconds)
+
+    workload = {2: "one MoE layer, 8-row verify window (4 slots x token+MTP proposal, Zipf(1.1) router prior, "
+                   "correlated pairs), hidden 2048, ffn 768, 128 experts top-8 + shared, 4-bit blocks of 32",
+                1: "one MoE layer, 4-row verify window (2 slots with MTP), hidden 2048, ffn 768, 128 experts top-8 "
+                   "+ shared, 4-bit blocks of 32",
+                4: f"one MoE layer, {R}-row window, hidden 4096, ffn 1024, 256 experts top-8 + shared, 2-bit "
+                   "blocks of 32"}[cfg.cid]
+    line = {
+        "metric": METRIC, "value": round(rows_s, 1), "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_total / K, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": workload, "config_id": cfg.cid, "rows": R, "hidden": H, "ffn": F, "experts": E,
+                   "top_k": cfg.top_k, "bits": cfg.bits, "layer_instances": args.layers},
+        "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "mean_distinct_experts": round(float(U.mean()), 2),
+        "unique_weight_bytes_per_window": round(bytes_total / K),
+        "kernel_us": {"route": round(1e3 * sum(d_route) / P, 3), "gateup": round(1e3 * sum(d_gu) / P, 3),
+                      "down": round(1e3 * sum(d_dn) / P, 3)},
+        "wall_s": round(wall, 4),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
+    """24 layers + head per step (the layer-stack workload)."""
+    cfg = synth.config(3)
+    K, W = min(args.steps, 256), min(args.warmup, 8)
+    R, H, F, E, k = cfg.rows, cfg.hidden, cfg.ffn, cfg.experts, cfg.top_k
+    t0 = time.time()
+    layers = []
+    for l in range(cfg.layers):
+        layers.append(DevLayer(synth.make_layer(cfg, l), cfg))
+        log(f"[bench] layer {l + 1}/{cfg.layers} resident ({time.time() - t0:.1f}s)")
+    codes, meta = synth.make_head(cfg)
+    head = sw.upload_qmat(codes, meta, cfg.vocab, H, 8)
+    xs = [to_dev_x(synth.make_window(cfg, w)) for w in range(16)]
+    routes = [sw.RouteOut(R, E, k) for _ in range(cfg.layers)]
+    ws_r = sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E))
+    ws_m = sw.workspace(sw.workspace_bytes(1, R, H, F, E, k))
+    ws_h = sw.workspace(sw.workspace_bytes(2, R, H, vocab=cfg.vocab))
+    xa = torch.empty(R, H, dtype=torch.bfloat16, device="cuda")
+    xb = torch.empty_like(xa)
+    out = torch.empty(R, H, dtype=torch.float32, device="cuda")
+    logits = torch.empty(R, cfg.vocab, dtype=torch.float32, device="cuda")
+    am = torch.empty(8, dtype=torch.int32, device="cuda")
+    n_act = torch.zeros(K, cfg.layers, dtype=torch.int32, device="cuda")
+
+    def step(i, record=True):
+        xa.copy_(xs[i % len(xs)])
+        cur, nxt = xa, xb
+        for l, dl in enumerate(layers):
+            ro = sw.strata_window_route(cur, dl.gate_w, dl.bias, k, out=routes[l], ws=ws_r)
+            sw.strata_window_moe(cur, dl.gate, dl.up, dl.down, *dl.sh, ro, residual=cur, out=out, x_next=nxt,
+                                 ws=ws_m)
+            if record:
+                n_act[i, l].copy_(ro.n_active[0])
+            cur, nxt = nxt, cur
+        sw.strata_window_head(cur, head, logits=logits, argmax=am, ws=ws_h)
+
+    for i in range(W):
+        step(i, record=False)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(K):
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    U = (n_act - 1).cpu().numpy()
+    b_x = 3 * F * H * bpw(cfg.bits)
+    b_h = cfg.vocab * H * (1 + 2 / 32)
+    bytes_total = float((4 * E * H + (U + 1) * b_x).sum() + K * b_h)
+    gbs = bytes_total / (ms * 1e-3) / 1e9
+    line = {"metric": METRIC, "value": round(R * K / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": K,
+            "warmup": W, "ms_per_step": round(ms / K, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "24 MoE layers (hidden 2048, ffn 768, 128 experts top-8 + shared, 4-bit) with "
+                                   "residual, then an 8-bit head of vocab 151936 with argmax, 8-row window",
+                       "config_id": 3},
+            "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "roofline": None, "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,11 +25,16 @@
  *   - Return value: 0 on success, or a negative status (below). On error nothing has
  *     been enqueued, except for STRATA_EHIP, where a launch failed;
  *     strata_window_last_error() then describes the failure (thread-local string).
- *   - Workspace `ws`: at least strata_window_workspace(...) bytes. Its first
- *     STRATA_WS_COUNTER_BYTES bytes hold completion counters that must be zero before
- *     the first call that uses the buffer (e.g. one hipMemset at allocation); every call
- *     returns them to zero when its work completes. Two calls whose work may overlap in
- *     time must not share a workspace.
+ *   - prof_events (last argument of each compute entry point): NULL, or an array of
+ *     hipEvent_t handles (created by the caller, timing enabled) that the dispatches
+ *     themselves record at the start and end of each kernel, for measuring kernel
+ *     durations: route {start of its first kernel, end of its last}; moe {gate/up
+ *     start, gate/up end, down start, end of the combine}; head {start, end}. A NULL
+ *     entry is skipped. Pass NULL while the stream is being captured into a graph.
+ *   - Workspace `ws`: at least strata_window_workspace(...) bytes of scratch (partial
+ *     sums and intermediates; the first STRATA_WS_COUNTER_BYTES bytes are reserved).
+ *     Its contents need no initialisation. Two calls whose work may overlap in time must
+ *     not share a workspace.
  *
  * Limits: 1 <= rows <= 8; 1 <= top_k <= 8; top_k <= n_experts <= 256.
  */
@@ -128,13 +133,12 @@ typedef struct {
  *   exact products; p = softmax over all experts; the top_k largest logits are selected.
  *   flags: 0 or STRATA_ROUTE_RENORM.
  * Errors: STRATA_EINVAL for a null or misaligned pointer, a bad dtype or flag, sizes
- * outside the limits, hidden % 64 != 0, or a workspace smaller than
- * strata_window_workspace(0, ...).
+ * outside the limits, or a workspace smaller than strata_window_workspace(0, ...).
  */
 int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int hidden,
                         const float* gate_w, const float* logit_bias, int n_experts,
                         int top_k, int flags, const strata_route_out* out,
-                        void* ws, size_t ws_bytes);
+                        void* ws, size_t ws_bytes, void* const* prof_events);
 
 /*
  * strata_window_moe - the experts of one window: for every active expert and each of its
@@ -160,7 +164,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
                       const strata_qmat* sh_up, const strata_qmat* sh_down,
                       const strata_route_out* route, int n_experts, int top_k,
                       const void* residual, float* out, uint16_t* x_next_bf16,
-                      void* ws, size_t ws_bytes);
+                      void* ws, size_t ws_bytes, void* const* prof_events);
 
 /*
  * strata_window_head - the output head of the window (Strata docs/BATCHING.md, opening
@@ -172,7 +176,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
  */
 int strata_window_head(void* stream, const void* x, int x_dtype, int rows, int hidden,
                        const strata_qmat* head, int vocab, float* logits,
-                       int32_t* argmax, void* ws, size_t ws_bytes);
+                       int32_t* argmax, void* ws, size_t ws_bytes, void* const* prof_events);
 
 /* Workspace bytes for which = 0 (route), 1 (moe), 2 (head); 0 for invalid arguments. */
 size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts,

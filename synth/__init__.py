@@ -91,10 +91,12 @@ def qmatrix(rng, n_mat, rows, cols, bits):
     assert rows % 16 == 0 and cols % (512 // bits) == 0
     nbytes = rows * cols * bits // 8
     nblk = rows * cols // 32
-    if bits == 8:
-        codes = rng.integers(-127, 128, size=(n_mat, nbytes), dtype=np.int16).astype(np.int8).view(np.uint8)
-    else:
-        codes = rng.integers(0, 256, size=(n_mat, nbytes), dtype=np.uint8)
+    codes = rng.integers(0, 256, size=(n_mat, nbytes), dtype=np.uint8)
+    if bits == 8:  # int8 uniform over [-127, 127]: redraw every -128
+        bad = np.flatnonzero(codes == 0x80)
+        while bad.size:
+            codes.flat[bad] = rng.integers(0, 256, size=bad.size, dtype=np.uint8)
+            bad = bad[codes.flat[bad] == 0x80]
     scale = (rng.uniform(0.75, 1.25, size=(n_mat, nblk)) / (_code_std(bits) * np.sqrt(cols))).astype(np.float16)
     if bits == 8:
         return codes, scale.view(np.uint16)

@@ -1,0 +1,189 @@
+"""GPU parity of the verify-window MoE layer against the CPU oracle, through the C ABI.
+
+Routing indices and per-expert row lists must match bit for bit; outputs must be within
+a per-row relative error of 2e-3 (float32 accumulation against the double-precision
+definition). A window's row must equal the same row computed alone, bit for bit (Strata
+docs/BATCHING.md, "Exactness").
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import verify_window_expert_amd as sw  # noqa: E402
+from gpu_helpers import (REL_TOL, DevLayer, assert_route_equal, gpu_window, oracle_mats,  # noqa: E402
+                         oracle_window, row_rel_err, to_dev_x, topk_gap)
+
+_layers = {}
+
+
+def layer_for(cfg, layer=0):
+    key = (cfg, layer)
+    if key not in _layers:
+        if len(_layers) > 6:
+            _layers.clear()
+        L = synth.make_layer(cfg, layer)
+        _layers[key] = (L, DevLayer(L, cfg), oracle_mats(L, cfg))
+    return _layers[key]
+
+
+def check_window(cfg, window=0, renorm=False, residual=False, x=None, x_next=False, ties=False):
+    L, dl, mats = layer_for(cfg)
+    x = synth.make_window(cfg, window) if x is None else x
+    print(f"[parity] cid={cfg.cid} H={cfg.hidden} F={cfg.ffn} E={cfg.experts} k={cfg.top_k} bits={cfg.bits} "
+          f"R={x.shape[0]} window={window} renorm={renorm} residual={residual}", flush=True)
+    gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next)
+    orc, oout, oxn = oracle_window(L, mats, x, cfg, renorm, residual, x_next)
+    # exact ties (equal logits) are decided identically by index; near-ties are not
+    # well-posed across summation orders, so a seed must not produce them
+    if not ties:
+        assert topk_gap(orc["logits"], cfg.top_k) > 1e-9, "near-tie in the routing of this seed"
+    assert_route_equal(gr, orc, cfg)
+    err = row_rel_err(gout, oout)
+    assert err <= REL_TOL, err
+    return gr, gout, oout, err, gxn, oxn
+
+
+# --------------------------------------------------------------------- the five configs
+
+@pytest.mark.parametrize("window", [0, 1])
+def test_config0_tiny(window):
+    check_window(synth.config(0), window)
+
+
+def test_config0_renorm_residual():
+    check_window(synth.config(0), 2, renorm=True, residual=True)
+
+
+@pytest.mark.parametrize("window", [0, 1])
+def test_config1_four_rows(window):
+    _, _, _, err, _, _ = check_window(synth.config(1), window)
+    print("config1 rel err", err)
+
+
+@pytest.mark.parametrize("window", [0, 1, 2])
+def test_config2_eight_rows_zipf_pairs(window):
+    _, _, _, err, _, _ = check_window(synth.config(2), window)
+    print("config2 rel err", err)
+
+
+@pytest.mark.parametrize("rows", synth.CONFIG4_ROWS)
+def test_config4_two_bit_row_sweep(rows):
+    cfg = synth.config(4, rows=rows)
+    check_window(cfg, 0)
+
+
+def test_x_next_is_bf16_of_output():
+    cfg = synth.config(1)
+    _, gout, oout, _, gxn, oxn = check_window(cfg, 3, residual=True, x_next=True)
+    gx = synth.bf16_bits_to_f32(gxn)
+    # x_next is the bf16 rounding of the GPU's own output
+    assert np.array_equal(gxn, synth.f32_to_bf16_bits(gout))
+    ox = synth.bf16_bits_to_f32(oxn)
+    # each side rounds its own output to bf16 (half an ulp: at most 2^-8 of the value),
+    # so the two may differ by those roundings plus the outputs' own difference
+    bound = 2.0 ** -8 * (np.abs(gout) + np.abs(oout)) + np.abs(gout - oout) + 1e-30
+    assert np.all(np.abs(gx.astype(np.float64) - ox) <= bound)
+
+
+# --------------------------------------------------------------------- shapes and edges
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_every_row_count(rows):
+    cfg = synth.config(0, rows=rows, top_k=3, experts=13)
+    check_window(cfg, 5)
+
+
+def test_ragged_shapes():
+    """Expert count not a multiple of the router's 4 experts per workgroup, hidden not a
+    multiple of its 512-input chunk, several output ranges, 2-bit."""
+    check_window(synth.config(0, hidden=640, ffn=384, experts=13, top_k=5, rows=7), 0)
+    check_window(synth.config(0, hidden=768, ffn=512, experts=10, top_k=4, rows=5, bits=2, x_dtype="bf16"), 1)
+
+
+def test_all_rows_share_experts():
+    cfg = synth.config(0, rows=8, top_k=4)
+    x = np.repeat(synth.make_window(cfg, 0)[:1], 8, axis=0)
+    gr, gout, _, _, _, _ = check_window(cfg, x=x)
+    assert gr["n_active"] == 4 + 1
+    assert np.all(gout == gout[0])
+
+
+def test_disjoint_rows():
+    cfg = synth.config(0, rows=8, top_k=2, experts=16)
+    L, dl, mats = layer_for(cfg)
+    x = np.zeros((8, cfg.hidden), np.float32)
+    # rows aligned with pairs of router rows so every row picks its own pair of experts
+    G = L.gate_w.astype(np.float64)
+    for r in range(8):
+        x[r] = (40.0 * (G[2 * r] + G[2 * r + 1]) / np.linalg.norm(G[2 * r] + G[2 * r + 1]) ** 2).astype(np.float32)
+    gr, _, _, _, _, _ = check_window(cfg, x=x)
+    assert gr["n_active"] == 16 + 1
+    assert sorted(gr["topk_idx"].ravel().tolist()) == list(range(16))
+
+
+def test_k_equals_e_full_mixture():
+    check_window(synth.config(0, experts=8, top_k=8, rows=3), 0, renorm=True)
+
+
+def test_zero_rows():
+    cfg = synth.config(0, rows=3)
+    x = synth.make_window(cfg, 0)
+    x[1] = 0.0
+    gr, gout, oout, _, _, _ = check_window(cfg, x=x, ties=True)
+    assert list(gr["topk_idx"][1]) == list(range(cfg.top_k))   # equal logits: lowest indices
+    assert np.all(gout[1] == 0.0)
+
+
+def test_max_limits():
+    """rows 8, k 8, 256 experts (the ABI's maxima), reduced width."""
+    check_window(synth.config(4, hidden=1024, ffn=256, rows=8), 0)
+
+
+# --------------------------------------------------------------------- invariance
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_window_row_equals_row_alone_bitwise(cid):
+    """Strata docs/BATCHING.md, "Exactness": a batch row's arithmetic is the single-token
+    window's. Each row of a full window equals that row run as a 1-row window, bit for bit."""
+    cfg = synth.config(cid)
+    L, dl, mats = layer_for(cfg)
+    x = synth.make_window(cfg, 7)
+    gr, gout, _ = gpu_window(dl, to_dev_x(x), cfg.top_k)
+    for r in range(cfg.rows):
+        g1, o1, _ = gpu_window(dl, to_dev_x(x[r:r + 1]), cfg.top_k)
+        assert np.array_equal(g1["topk_idx"][0], gr["topk_idx"][r])
+        assert np.array_equal(o1[0], gout[r]), (r, np.max(np.abs(o1[0] - gout[r])))
+
+
+def test_run_to_run_deterministic():
+    cfg = synth.config(2)
+    L, dl, mats = layer_for(cfg)
+    xd = to_dev_x(synth.make_window(cfg, 4))
+    ref = gpu_window(dl, xd, cfg.top_k)[1]
+    for _ in range(20):
+        assert np.array_equal(gpu_window(dl, xd, cfg.top_k)[1], ref)
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, filled with garbage first (it needs no initialisation), serves
+    windows of different row counts back to back."""
+    cfg = synth.config(2)
+    L, dl, mats = layer_for(cfg)
+    ws_r = sw.workspace(sw.workspace_bytes(0, 8, cfg.hidden, n_experts=cfg.experts)).fill_(0xA5)
+    ws_m = sw.workspace(sw.workspace_bytes(1, 8, cfg.hidden, cfg.ffn, cfg.experts, cfg.top_k)).fill_(0xFF)
+    for rows in (8, 3, 8, 1):
+        x = synth.make_window(cfg, 9)[:rows]
+        xd = to_dev_x(x)
+        ro = sw.strata_window_route(xd, dl.gate_w, dl.bias, cfg.top_k, ws=ws_r)
+        out = sw.strata_window_moe(xd, dl.gate, dl.up, dl.down, *dl.sh, ro, ws=ws_m)
+        torch.cuda.synchronize()
+        _, o2, _ = gpu_window(dl, xd, cfg.top_k)
+        assert np.array_equal(out.cpu().numpy(), o2)

@@ -1,0 +1,235 @@
+"""Python binding of libstrata_window.so, the verify-window MoE layer for gfx950.
+
+Argument marshalling only: every step of the layer runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream. The entry points keep the C
+names (strata_window_route / strata_window_moe / strata_window_head); their contracts
+are in include/strata_window.h. If the library has not been built, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH, build  # noqa: F401  (build() compiles the library)
+
+STRATA_OK, STRATA_EINVAL, STRATA_EUNSUPPORTED, STRATA_EHIP = 0, -1, -2, -3
+STRATA_F32, STRATA_BF16 = 0, 1
+STRATA_ROUTE_RENORM = 1
+MAX_ROWS, MAX_TOPK, MAX_EXPERTS = 8, 8, 256
+WS_COUNTER_BYTES = 4096
+
+
+class StrataError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"strata_window status {status}: {message}")
+        self.status = status
+
+
+class CQMat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("n_mat", ctypes.c_int32),
+                ("mat_stride_codes", ctypes.c_int64), ("mat_stride_meta", ctypes.c_int64)]
+
+
+class CRouteOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "n_active", "active", "offsets", "entry_row", "entry_w", "row_mask")]
+
+
+_lib = None
+
+
+def library():
+    """The loaded library (ctypes.CDLL). Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: call verify_window_expert_amd.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.strata_window_route.argtypes = [P, P, I, I, I, P, P, I, I, I, ctypes.POINTER(CRouteOut), P, S, P]
+        L.strata_window_route.restype = I
+        L.strata_window_moe.argtypes = [P, P, I, I, I, I] + [ctypes.POINTER(CQMat)] * 6 + \
+            [ctypes.POINTER(CRouteOut), I, I, P, P, P, P, S, P]
+        L.strata_window_moe.restype = I
+        L.strata_window_head.argtypes = [P, P, I, I, I, ctypes.POINTER(CQMat), I, P, P, P, S, P]
+        L.strata_window_head.restype = I
+        L.strata_window_workspace.argtypes = [I, I, I, I, I, I, I]
+        L.strata_window_workspace.restype = S
+        L.strata_window_last_error.argtypes = []
+        L.strata_window_last_error.restype = ctypes.c_char_p
+        L.strata_window_abi_version.argtypes = []
+        L.strata_window_abi_version.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != STRATA_OK:
+        raise StrataError(status, library().strata_window_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _events(prof):
+    """ctypes array of hipEvent_t handles (ints) for the prof_events argument, or None."""
+    if prof is None:
+        return None
+    arr = (ctypes.c_void_p * len(prof))(*[p or None for p in prof])
+    return arr
+
+
+def _x_dtype(x):
+    if x.dtype == torch.float32:
+        return STRATA_F32
+    if x.dtype == torch.bfloat16:
+        return STRATA_BF16
+    raise TypeError("activations must be float32 or bfloat16")
+
+
+def _need(t, name, device=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class QMat:
+    """Device view of one block-quantized matrix, or n_mat stacked ones.
+
+    codes: uint8 tensor [n_mat, rows*cols*bits/8] in the documented chunk layout;
+    meta: int32 (scale | min << 16) or int16 (8-bit scale) tensor [n_mat, rows*cols/32].
+    """
+
+    def __init__(self, codes, meta, rows, cols, bits):
+        self.codes = _need(codes, "codes")
+        self.meta = _need(meta, "meta")
+        self.rows, self.cols, self.bits = int(rows), int(cols), int(bits)
+        self.n_mat = codes.shape[0] if codes.dim() == 2 else 1
+
+    def c(self):
+        per_c = self.codes.numel() // self.n_mat
+        per_m = self.meta.numel() // self.n_mat
+        return CQMat(self.codes.data_ptr(), self.meta.data_ptr(), self.rows, self.cols, self.bits,
+                     self.n_mat, per_c, per_m)
+
+
+def upload_qmat(codes, meta, rows, cols, bits, device="cuda"):
+    """QMat from NumPy arrays (codes uint8, meta uint32/uint16) copied to the device."""
+    import numpy as np
+    c = torch.from_numpy(np.ascontiguousarray(codes)).to(device)
+    m = np.ascontiguousarray(meta)
+    m = torch.from_numpy(m.view(np.int32) if m.dtype == np.uint32 else m.view(np.int16)).to(device)
+    if c.dim() == 1:
+        c, m = c.unsqueeze(0), m.unsqueeze(0)
+    return QMat(c, m, rows, cols, bits)
+
+
+class RouteOut:
+    """Device tensors of one window's routing (see strata_route_out)."""
+
+    def __init__(self, rows, n_experts, top_k, device="cuda"):
+        i32 = dict(dtype=torch.int32, device=device)
+        A = min(n_experts, rows * top_k) + 1
+        ent = rows * top_k + rows
+        self.rows, self.n_experts, self.top_k = rows, n_experts, top_k
+        self.topk_idx = torch.empty(rows * top_k, **i32)
+        self.topk_w = torch.empty(rows * top_k, dtype=torch.float32, device=device)
+        self.n_active = torch.empty(4, **i32)
+        self.active = torch.empty(A, **i32)
+        self.offsets = torch.empty(A + 1, **i32)
+        self.entry_row = torch.empty(ent, **i32)
+        self.entry_w = torch.empty(ent, dtype=torch.float32, device=device)
+        self.row_mask = torch.empty(n_experts + 1, dtype=torch.uint8, device=device)
+
+    def c(self):
+        return CRouteOut(*(t.data_ptr() for t in (self.topk_idx, self.topk_w, self.n_active, self.active,
+                                                   self.offsets, self.entry_row, self.entry_w, self.row_mask)))
+
+    def host(self):
+        """Copy to the host as NumPy arrays, cut to the active length."""
+        n = int(self.n_active[0].item())
+        off = self.offsets[:n + 1].cpu().numpy()
+        e = int(off[-1])
+        return dict(topk_idx=self.topk_idx.view(self.rows, self.top_k).cpu().numpy(),
+                    topk_w=self.topk_w.view(self.rows, self.top_k).cpu().numpy(),
+                    n_active=n, active=self.active[:n].cpu().numpy(), offsets=off,
+                    entry_row=self.entry_row[:e].cpu().numpy(), entry_w=self.entry_w[:e].cpu().numpy(),
+                    row_mask=self.row_mask.cpu().numpy())
+
+
+def workspace_bytes(which, rows, hidden, ffn=0, n_experts=0, top_k=0, vocab=0):
+    return library().strata_window_workspace(which, rows, hidden, ffn, n_experts, top_k, vocab)
+
+
+def workspace(nbytes, device="cuda"):
+    """A zeroed device workspace (its completion counters must start at zero)."""
+    return torch.zeros(max(int(nbytes), WS_COUNTER_BYTES), dtype=torch.uint8, device=device)
+
+
+def strata_window_route(x, gate_w, bias, top_k, renorm=False, out=None, ws=None, stream=None, prof=None):
+    """Router, softmax, top-k and grouping of one window. Returns a RouteOut.
+    prof: None or [start, end] hipEvent_t handles recorded around the kernel."""
+    _need(x, "x"); _need(gate_w, "gate_w")
+    if bias is not None:
+        _need(bias, "bias")
+    rows, hidden = x.shape
+    E = gate_w.shape[0]
+    out = RouteOut(rows, E, top_k, x.device) if out is None else out
+    if ws is None:
+        ws = workspace(workspace_bytes(0, rows, hidden, n_experts=E), x.device)
+    ro = out.c()
+    _check(library().strata_window_route(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, _ptr(gate_w),
+                                         _ptr(bias), E, top_k, STRATA_ROUTE_RENORM if renorm else 0,
+                                         ctypes.byref(ro), _ptr(ws), ws.numel(), _events(prof)))
+    return out
+
+
+def strata_window_moe(x, gate, up, down, sh_gate, sh_up, sh_down, route, residual=None, out=None,
+                      x_next=None, ws=None, stream=None, prof=None):
+    """Experts of one window. Returns out [rows, hidden] float32 (x_next filled if given).
+    prof: None or [gate/up start, gate/up end, down start, down end] hipEvent_t handles."""
+    _need(x, "x")
+    rows, hidden = x.shape
+    ffn = gate.rows
+    if out is None:
+        out = torch.empty(rows, hidden, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(workspace_bytes(1, rows, hidden, ffn, route.n_experts, route.top_k), x.device)
+    if residual is not None:
+        _need(residual, "residual")
+    if x_next is not None:
+        _need(x_next, "x_next")
+    qs = [q.c() for q in (gate, up, down, sh_gate, sh_up, sh_down)]
+    ro = route.c()
+    _check(library().strata_window_moe(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ffn,
+                                       *[ctypes.byref(q) for q in qs], ctypes.byref(ro), route.n_experts,
+                                       route.top_k, _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws),
+                                       ws.numel(), _events(prof)))
+    return out
+
+
+def strata_window_head(x, head, logits=True, argmax=None, ws=None, stream=None, prof=None):
+    """Head GEMV and argmax of one window. Returns (logits or None, argmax int32 [rows])."""
+    _need(x, "x")
+    rows, hidden = x.shape
+    V = head.rows
+    lg = torch.empty(rows, V, dtype=torch.float32, device=x.device) if logits is True else logits
+    if lg is False:
+        lg = None
+    am = torch.empty(max(rows, 4), dtype=torch.int32, device=x.device) if argmax is None else argmax
+    if ws is None:
+        ws = workspace(workspace_bytes(2, rows, hidden, vocab=V), x.device)
+    q = head.c()
+    _check(library().strata_window_head(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ctypes.byref(q),
+                                        V, _ptr(lg), _ptr(am), _ptr(ws), ws.numel(), _events(prof)))
+    return lg, am[:rows]

@@ -1,0 +1,261 @@
+// C ABI of the verify-window MoE layer: argument checks, workspace layout, launches.
+// The entry points and their contracts are documented in include/strata_window.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "../../include/strata_window.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr size_t kLdsLimit = 160 * 1024;
+
+// ---------------------------------------------------------------- workspace layouts
+
+struct RouteWs { size_t partials, total; };
+RouteWs route_ws(int rows, int hidden, int E) {
+  const size_t n_hc = (hidden + 511) / 512;
+  RouteWs w;
+  w.partials = STRATA_WS_COUNTER_BYTES;
+  w.total = round_up(w.partials + sizeof(double) * rows * E * n_hc, 256);
+  return w;
+}
+
+struct MoeWs { size_t h, y, total; };
+MoeWs moe_ws(int rows, int hidden, int ffn, int top_k) {
+  const size_t ent = (size_t)rows * top_k + rows;
+  MoeWs w;
+  w.h = STRATA_WS_COUNTER_BYTES;
+  w.y = round_up(w.h + 4 * ent * ffn, 256);
+  w.total = round_up(w.y + 4 * ent * hidden, 256);
+  return w;
+}
+
+struct HeadWs { size_t val, idx, total; };
+HeadWs head_ws(int rows, int vocab) {
+  const size_t n = (size_t)sw::head_workgroups(vocab) * rows;
+  HeadWs w;
+  w.val = STRATA_WS_COUNTER_BYTES;
+  w.idx = round_up(w.val + 4 * n, 256);
+  w.total = round_up(w.idx + 4 * n, 256);
+  return w;
+}
+
+// ------------------------------------------------------------------------ checks
+
+int check_common(const void* x, int x_dtype, int rows, int hidden, void* ws) {
+  if (!x) return fail(STRATA_EINVAL, "x is NULL");
+  if (!aligned(x, 16)) return fail(STRATA_EINVAL, "x is not 16-byte aligned");
+  if (x_dtype != STRATA_F32 && x_dtype != STRATA_BF16) return fail(STRATA_EINVAL, "bad x_dtype %d", x_dtype);
+  if (rows < 1 || rows > STRATA_MAX_ROWS) return fail(STRATA_EINVAL, "rows %d outside 1..%d", rows, STRATA_MAX_ROWS);
+  if (hidden < 1) return fail(STRATA_EINVAL, "hidden %d < 1", hidden);
+  if (!ws) return fail(STRATA_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(STRATA_EINVAL, "workspace is not 256-byte aligned");
+  return STRATA_OK;
+}
+
+int check_experts(int n_experts, int top_k) {
+  if (top_k < 1 || top_k > STRATA_MAX_TOPK) return fail(STRATA_EINVAL, "top_k %d outside 1..%d", top_k, STRATA_MAX_TOPK);
+  if (n_experts < top_k || n_experts > STRATA_MAX_EXPERTS)
+    return fail(STRATA_EINVAL, "n_experts %d outside top_k..%d", n_experts, STRATA_MAX_EXPERTS);
+  return STRATA_OK;
+}
+
+int check_route_out(const strata_route_out* o) {
+  if (!o) return fail(STRATA_EINVAL, "route output descriptor is NULL");
+  const void* p[] = {o->topk_idx, o->topk_w, o->n_active, o->active, o->offsets, o->entry_row, o->entry_w, o->row_mask};
+  const char* nm[] = {"topk_idx", "topk_w", "n_active", "active", "offsets", "entry_row", "entry_w", "row_mask"};
+  for (int i = 0; i < 8; i++) {
+    if (!p[i]) return fail(STRATA_EINVAL, "route output %s is NULL", nm[i]);
+    if (!aligned(p[i], 16)) return fail(STRATA_EINVAL, "route output %s is not 16-byte aligned", nm[i]);
+  }
+  return STRATA_OK;
+}
+
+int check_qmat(const strata_qmat* q, const char* name, int rows, int cols, int n_mat, int bits) {
+  if (!q) return fail(STRATA_EINVAL, "%s descriptor is NULL", name);
+  if (!q->codes || !q->meta) return fail(STRATA_EINVAL, "%s codes/meta NULL", name);
+  if (!aligned(q->codes, 16) || !aligned(q->meta, 16)) return fail(STRATA_EINVAL, "%s codes/meta not 16-byte aligned", name);
+  if (q->bits != bits) return fail(STRATA_EINVAL, "%s has %d bits, expected %d", name, q->bits, bits);
+  if (q->rows != rows || q->cols != cols)
+    return fail(STRATA_EINVAL, "%s is %dx%d, expected %dx%d", name, q->rows, q->cols, rows, cols);
+  if (q->n_mat != n_mat) return fail(STRATA_EINVAL, "%s holds %d matrices, expected %d", name, q->n_mat, n_mat);
+  const int G = 512 / bits;
+  if (rows % 16 || cols % G) return fail(STRATA_EINVAL, "%s: rows %% 16 and cols %% %d must be 0", name, G);
+  if (n_mat > 1) {
+    const int64_t need_c = (int64_t)rows * cols * bits / 8, need_m = (int64_t)rows * (cols / 32);
+    if (q->mat_stride_codes < need_c || q->mat_stride_meta < need_m)
+      return fail(STRATA_EINVAL, "%s matrix strides smaller than one matrix", name);
+    const int64_t meta_bytes = q->mat_stride_meta * (bits == 8 ? 2 : 4);
+    if (q->mat_stride_codes % 16 || meta_bytes % 16)
+      return fail(STRATA_EINVAL, "%s matrix strides break 16-byte alignment", name);
+  }
+  return STRATA_OK;
+}
+
+int launch_status(int rc, const char* what) {
+  if (rc == 0) return STRATA_OK;
+  return fail(STRATA_EHIP, "%s launch failed: %s", what, hipGetErrorString((hipError_t)rc));
+}
+
+sw::Prof prof(void* const* ev, int i) {
+  sw::Prof p;
+  if (ev) {
+    p.start = (hipEvent_t)ev[i];
+    p.stop = (hipEvent_t)ev[i + 1];
+  }
+  return p;
+}
+
+sw::QDev qdev(const strata_qmat* routed, const strata_qmat* shared) {
+  sw::QDev d;
+  d.codes = (const uint8_t*)routed->codes;
+  d.meta = (const uint8_t*)routed->meta;
+  d.stride_codes = routed->mat_stride_codes;
+  d.stride_meta_bytes = routed->mat_stride_meta * (routed->bits == 8 ? 2 : 4);
+  d.sh_codes = (const uint8_t*)shared->codes;
+  d.sh_meta = (const uint8_t*)shared->meta;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int strata_window_abi_version(void) { return STRATA_WINDOW_ABI_VERSION; }
+
+const char* strata_window_last_error(void) { return g_err; }
+
+size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts, int top_k, int vocab) {
+  if (rows < 1 || rows > STRATA_MAX_ROWS || hidden < 1) return 0;
+  switch (which) {
+    case 0: return n_experts >= 1 ? route_ws(rows, hidden, n_experts).total : 0;
+    case 1: return (ffn >= 1 && top_k >= 1) ? moe_ws(rows, hidden, ffn, top_k).total : 0;
+    case 2: return vocab >= 1 ? head_ws(rows, vocab).total : 0;
+    default: return 0;
+  }
+}
+
+int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int hidden, const float* gate_w,
+                        const float* logit_bias, int n_experts, int top_k, int flags, const strata_route_out* out,
+                        void* ws, size_t ws_bytes, void* const* prof_events) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_common(x, x_dtype, rows, hidden, ws))) return rc;
+  if ((rc = check_experts(n_experts, top_k))) return rc;
+  if (!gate_w || !aligned(gate_w, 16)) return fail(STRATA_EINVAL, "gate_w NULL or not 16-byte aligned");
+  if (logit_bias && !aligned(logit_bias, 16)) return fail(STRATA_EINVAL, "logit_bias not 16-byte aligned");
+  if (flags & ~STRATA_ROUTE_RENORM) return fail(STRATA_EINVAL, "unknown route flags 0x%x", flags);
+  if ((rc = check_route_out(out))) return rc;
+  const RouteWs w = route_ws(rows, hidden, n_experts);
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "route workspace %zu < %zu bytes", ws_bytes, w.total);
+
+  sw::RouteArgs a;
+  a.x = x; a.x_dtype = x_dtype; a.rows = rows; a.hidden = hidden;
+  a.gate_w = gate_w; a.bias = logit_bias; a.n_experts = n_experts; a.top_k = top_k;
+  a.renorm = (flags & STRATA_ROUTE_RENORM) != 0;
+  a.partials = (double*)((char*)ws + w.partials);
+  a.topk_idx = out->topk_idx; a.topk_w = out->topk_w; a.n_active = out->n_active; a.active = out->active;
+  a.offsets = out->offsets; a.entry_row = out->entry_row; a.entry_w = out->entry_w; a.row_mask = out->row_mask;
+  const sw::Prof pr = prof(prof_events, 0);
+  return launch_status(sw::launch_route(a, (hipStream_t)stream, prof_events ? &pr : nullptr), "route");
+}
+
+int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
+                      const strata_qmat* gate, const strata_qmat* up, const strata_qmat* down,
+                      const strata_qmat* sh_gate, const strata_qmat* sh_up, const strata_qmat* sh_down,
+                      const strata_route_out* route, int n_experts, int top_k, const void* residual, float* out,
+                      uint16_t* x_next_bf16, void* ws, size_t ws_bytes, void* const* prof_events) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_common(x, x_dtype, rows, hidden, ws))) return rc;
+  if ((rc = check_experts(n_experts, top_k))) return rc;
+  if (ffn < 1) return fail(STRATA_EINVAL, "ffn %d < 1", ffn);
+  if ((rc = check_route_out(route))) return rc;
+  if (!gate) return fail(STRATA_EINVAL, "gate descriptor is NULL");
+  const int bits = gate->bits;
+  if (bits == 8) return fail(STRATA_EUNSUPPORTED, "8-bit expert matrices are not built (4 or 2 bits)");
+  if (bits != 4 && bits != 2) return fail(STRATA_EINVAL, "expert bits %d not in {2, 4}", bits);
+  if ((rc = check_qmat(gate, "gate", ffn, hidden, n_experts, bits))) return rc;
+  if ((rc = check_qmat(up, "up", ffn, hidden, n_experts, bits))) return rc;
+  if ((rc = check_qmat(down, "down", hidden, ffn, n_experts, bits))) return rc;
+  if ((rc = check_qmat(sh_gate, "sh_gate", ffn, hidden, 1, bits))) return rc;
+  if ((rc = check_qmat(sh_up, "sh_up", ffn, hidden, 1, bits))) return rc;
+  if ((rc = check_qmat(sh_down, "sh_down", hidden, ffn, 1, bits))) return rc;
+  if (!out || !aligned(out, 16)) return fail(STRATA_EINVAL, "out NULL or not 16-byte aligned");
+  if (residual && !aligned(residual, 16)) return fail(STRATA_EINVAL, "residual not 16-byte aligned");
+  if (x_next_bf16 && !aligned(x_next_bf16, 16)) return fail(STRATA_EINVAL, "x_next not 16-byte aligned");
+  const size_t lds_gu = (size_t)(x_dtype == STRATA_F32 ? 16 : 8) * (hidden + 8) * 2 + (size_t)(hidden / 32) * 64;
+  const size_t lds_dn = (size_t)16 * (ffn + 8) * 2 + (size_t)(ffn / 32) * 64;
+  if (lds_gu > kLdsLimit || lds_dn > kLdsLimit)
+    return fail(STRATA_EUNSUPPORTED, "hidden %d / ffn %d need more than %zu bytes of LDS", hidden, ffn, kLdsLimit);
+  const MoeWs w = moe_ws(rows, hidden, ffn, top_k);
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "moe workspace %zu < %zu bytes", ws_bytes, w.total);
+  const int n_ranges = sw::down_ranges(hidden);
+
+  const int max_slots = std::min(n_experts, rows * top_k) + 1;
+  hipStream_t s = (hipStream_t)stream;
+
+  sw::GateUpArgs g;
+  g.x = x; g.x_dtype = x_dtype; g.rows = rows; g.hidden = hidden; g.ffn = ffn; g.bits = bits;
+  g.n_experts = n_experts;
+  g.gate = qdev(gate, sh_gate); g.up = qdev(up, sh_up);
+  g.n_active = route->n_active; g.active = route->active; g.offsets = route->offsets; g.entry_row = route->entry_row;
+  g.row_mask = route->row_mask;
+  g.max_slots = max_slots;
+  g.h = (float*)((char*)ws + w.h);
+  const sw::Prof pg = prof(prof_events, 0), pd = prof(prof_events, 2);
+  if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
+
+  sw::DownArgs d;
+  d.x_res = residual; d.x_dtype = x_dtype; d.rows = rows; d.hidden = hidden; d.ffn = ffn; d.bits = bits;
+  d.n_experts = n_experts;
+  d.down = qdev(down, sh_down);
+  d.n_active = route->n_active; d.active = route->active; d.offsets = route->offsets;
+  d.entry_row = route->entry_row; d.entry_w = route->entry_w; d.row_mask = route->row_mask;
+  d.h = g.h; d.y = (float*)((char*)ws + w.y); d.out = out; d.x_next = x_next_bf16;
+  d.n_ranges = n_ranges; d.max_slots = max_slots; d.top_k = top_k;
+  return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
+}
+
+int strata_window_head(void* stream, const void* x, int x_dtype, int rows, int hidden, const strata_qmat* head,
+                       int vocab, float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
+                       void* const* prof_events) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_common(x, x_dtype, rows, hidden, ws))) return rc;
+  if (vocab < 1) return fail(STRATA_EINVAL, "vocab %d < 1", vocab);
+  if ((rc = check_qmat(head, "head", vocab, hidden, 1, 8))) return rc;
+  if (!argmax || !aligned(argmax, 16)) return fail(STRATA_EINVAL, "argmax NULL or not 16-byte aligned");
+  if (logits && !aligned(logits, 16)) return fail(STRATA_EINVAL, "logits not 16-byte aligned");
+  const size_t lds = (size_t)(x_dtype == STRATA_F32 ? 16 : 8) * (hidden + 8) * 2 + (size_t)(hidden / 32) * 64;
+  if (lds > kLdsLimit) return fail(STRATA_EUNSUPPORTED, "hidden %d needs more than %zu bytes of LDS", hidden, kLdsLimit);
+  const HeadWs w = head_ws(rows, vocab);
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "head workspace %zu < %zu bytes", ws_bytes, w.total);
+
+  sw::HeadArgs a;
+  a.x = x; a.x_dtype = x_dtype; a.rows = rows; a.hidden = hidden; a.vocab = vocab;
+  a.codes = (const uint8_t*)head->codes; a.meta = (const uint8_t*)head->meta;
+  a.logits = logits; a.argmax = argmax;
+  a.part_val = (float*)((char*)ws + w.val); a.part_idx = (int32_t*)((char*)ws + w.idx);
+  const sw::Prof ph = prof(prof_events, 0);
+  return launch_status(sw::launch_head(a, (hipStream_t)stream, prof_events ? &ph : nullptr), "head");
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Kernel argument blocks and launchers of the window kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <stdint.h>
+
+namespace sw {
+
+struct RouteArgs {
+  const void* x; int x_dtype; int rows, hidden;
+  const float* gate_w; const float* bias; int n_experts, top_k, renorm;
+  double* partials;         // [chunk][row][expert]
+  int32_t* topk_idx; float* topk_w; int32_t* n_active; int32_t* active; int32_t* offsets;
+  int32_t* entry_row; float* entry_w; uint8_t* row_mask;
+};
+
+// One quantized matrix family: routed experts (stacked) and the shared expert.
+struct QDev {
+  const uint8_t* codes; const uint8_t* meta;      // routed, matrix 0
+  int64_t stride_codes, stride_meta_bytes;        // between routed matrices
+  const uint8_t* sh_codes; const uint8_t* sh_meta;
+};
+
+struct GateUpArgs {
+  const void* x; int x_dtype; int rows, hidden, ffn, bits, n_experts;
+  QDev gate, up;
+  const int32_t* n_active; const int32_t* active; const int32_t* offsets;
+  const int32_t* entry_row; const uint8_t* row_mask;
+  float* h;                 // [entries][ffn]
+  int max_slots;            // capacity of the active array (offsets: max_slots + 1)
+};
+
+struct DownArgs {
+  const void* x_res; int x_dtype; int rows, hidden, ffn, bits, n_experts;
+  QDev down;
+  const int32_t* n_active; const int32_t* active; const int32_t* offsets;
+  const int32_t* entry_row; const float* entry_w; const uint8_t* row_mask;
+  const float* h;           // [entries][ffn]
+  float* y;                 // [entries][hidden]
+  float* out; uint16_t* x_next;
+  int n_ranges;             // 64-row output ranges
+  int max_slots, top_k;     // capacity of the active / offsets arrays; routing top-k
+};
+
+struct HeadArgs {
+  const void* x; int x_dtype; int rows, hidden, vocab;
+  const uint8_t* codes; const uint8_t* meta;
+  float* logits;            // nullable
+  int32_t* argmax;
+  float* part_val; int32_t* part_idx;   // [workgroups][rows]
+};
+
+// Optional timing events of one launch (both may be null): recorded by the dispatch
+// itself at the kernel's start and end (hipExtLaunchKernel).
+struct Prof {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Launch `kernel`, with the dispatch recording `p`'s events when given.
+template <typename K, typename... Args>
+inline void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Prof* p, Args... args) {
+  if (p && (p->start || p->stop))
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, p->start, p->stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
+
+// Launchers return the hipError_t of the launch (0 on success).
+int launch_route(const RouteArgs& a, hipStream_t s, const Prof* p);
+int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
+int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p);
+int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
+int head_workgroups(int vocab);
+int down_ranges(int hidden);
+
+}  // namespace sw
