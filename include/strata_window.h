@@ -55,6 +55,7 @@ enum { STRATA_F32 = 0, STRATA_BF16 = 1 };       /* activation dtypes            
 enum { STRATA_ROUTE_RENORM = 1 };                /* route flag: divide top-k weights
                                                     by their sum                     */
 enum { STRATA_MAX_ROWS = 8, STRATA_MAX_TOPK = 8, STRATA_MAX_EXPERTS = 256 };
+enum { STRATA_MAX_FFN = 4096 };                  /* strata_window_moe: widest ffn    */
 #define STRATA_WS_COUNTER_BYTES 4096
 
 /*
@@ -156,7 +157,10 @@ int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int 
  *   x_next_bf16 NULL or [rows][hidden] bf16: round-to-nearest-even of out
  * Intermediates stay in float. Bits 4 or 2 (all six matrices alike).
  * Errors: STRATA_EINVAL as for route, or mismatched matrix shapes/bits, or a workspace
- * smaller than strata_window_workspace(1, ...); STRATA_EUNSUPPORTED for bits 8 here.
+ * smaller than strata_window_workspace(1, ...); STRATA_EUNSUPPORTED for bits 8 here, for
+ * ffn > STRATA_MAX_FFN, or for a hidden / ffn whose activation image does not fit one
+ * compute unit's 160 KB of LDS (about hidden <= 7936 for bf16 x, <= 4480 for float x,
+ * ffn <= 4096).
  */
 int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hidden,
                       int ffn, const strata_qmat* gate, const strata_qmat* up,

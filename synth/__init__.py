@@ -19,7 +19,13 @@ prompts). These generators stand in for them with the shapes of five configurati
 Value recipe (not from the pages; chosen so activations stay O(1) through 24 layers and
 the dequantised weights are exact in float32):
   codes:  uniform over all codes (random bytes for 2/4-bit; int8 uniform in [-127, 127])
-  scale:  binary16( U(0.75, 1.25) / (sigma_q * sqrt(cols)) ), sigma_q = std of the code
+  scale:  binary16( g * U(0.75, 1.25) / (sigma_q * sqrt(cols)) ), sigma_q = std of the code,
+          g = 1, except g = 1/4 for the down projections of the 24-layer stack: every
+          matrix then has unit gain, and the layer's output grows with the square of its
+          input (silu(gate x) * up x), so with g = 1 a stack whose x_next feeds the next
+          layer overflows float32 by layer 10; with 1/4 the stream's rms goes 1.0 -> 1.6
+          over 24 layers (the models on the pages normalise each layer's input; that
+          dense part is outside this layer)
   min:    binary16( -scale * (2^bits - 1) / 2 )      (affine formats only)
   router: float32 N(0, 0.02);  bias (cid 2): -1.1 * ln(rank_e), rank a random permutation
   x:      N(0, 1); cid 2 rows (2s, 2s+1): x_p = 0.9 x_t + sqrt(0.19) z; then bf16 (RNE)
@@ -83,11 +89,11 @@ def _code_std(bits):
     return float(np.sqrt((n * n - 1) / 12.0))
 
 
-def qmatrix(rng, n_mat, rows, cols, bits):
+def qmatrix(rng, n_mat, rows, cols, bits, gain=1.0):
     """Random quantized matrices: codes uint8 [n_mat, rows*cols*bits/8] and meta
     ([n_mat, rows*cols/32], uint32 scale|min<<16 for 2/4-bit, uint16 scale for 8-bit).
     Every code and every block's (scale, min) is drawn independently, so the arrays do
-    not depend on where the layout puts each weight."""
+    not depend on where the layout puts each weight. gain multiplies every scale."""
     assert rows % 16 == 0 and cols % (512 // bits) == 0
     nbytes = rows * cols * bits // 8
     nblk = rows * cols // 32
@@ -97,7 +103,7 @@ def qmatrix(rng, n_mat, rows, cols, bits):
         while bad.size:
             codes.flat[bad] = rng.integers(0, 256, size=bad.size, dtype=np.uint8)
             bad = bad[codes.flat[bad] == 0x80]
-    scale = (rng.uniform(0.75, 1.25, size=(n_mat, nblk)) / (_code_std(bits) * np.sqrt(cols))).astype(np.float16)
+    scale = (gain * rng.uniform(0.75, 1.25, size=(n_mat, nblk)) / (_code_std(bits) * np.sqrt(cols))).astype(np.float16)
     if bits == 8:
         return codes, scale.view(np.uint16)
     mn = (-scale.astype(np.float64) * ((1 << bits) - 1) / 2.0).astype(np.float16)
@@ -133,12 +139,13 @@ def make_layer(cfg, layer=0):
     E, H, F, b = cfg.experts, cfg.hidden, cfg.ffn, cfg.bits
     gate_w, bias = make_router(cfg, layer)
     r_exp, r_sh = _rng(cfg.cid, 1, layer, 1), _rng(cfg.cid, 1, layer, 2)
+    g_down = 0.25 if cfg.layers > 1 else 1.0   # the stack's down gain (module docstring)
     gate = qmatrix(r_exp, E, F, H, b)
     up = qmatrix(r_exp, E, F, H, b)
-    down = qmatrix(r_exp, E, H, F, b)
+    down = qmatrix(r_exp, E, H, F, b, g_down)
     sh_gate = qmatrix(r_sh, 1, F, H, b)
     sh_up = qmatrix(r_sh, 1, F, H, b)
-    sh_down = qmatrix(r_sh, 1, H, F, b)
+    sh_down = qmatrix(r_sh, 1, H, F, b, g_down)
     return Layer(gate_w, bias, gate, up, down, sh_gate, sh_up, sh_down)
 
 

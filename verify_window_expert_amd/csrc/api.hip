@@ -25,6 +25,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr size_t kLdsLimit = 160 * 1024;
+constexpr size_t kStaticLds = 2048;   // the kernels' own tables (upper bound)
 
 // ---------------------------------------------------------------- workspace layouts
 
@@ -201,10 +202,10 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   if (!out || !aligned(out, 16)) return fail(STRATA_EINVAL, "out NULL or not 16-byte aligned");
   if (residual && !aligned(residual, 16)) return fail(STRATA_EINVAL, "residual not 16-byte aligned");
   if (x_next_bf16 && !aligned(x_next_bf16, 16)) return fail(STRATA_EINVAL, "x_next not 16-byte aligned");
-  const size_t lds_gu = (size_t)(x_dtype == STRATA_F32 ? 16 : 8) * (hidden + 8) * 2 + (size_t)(hidden / 32) * 64;
-  const size_t lds_dn = (size_t)16 * (ffn + 8) * 2 + (size_t)(ffn / 32) * 64;
-  if (lds_gu > kLdsLimit || lds_dn > kLdsLimit)
+  const size_t lds_gu = sw::gateup_lds_bytes(hidden, x_dtype), lds_dn = sw::down_lds_bytes(ffn);
+  if (lds_gu + kStaticLds > kLdsLimit || lds_dn + kStaticLds > kLdsLimit)
     return fail(STRATA_EUNSUPPORTED, "hidden %d / ffn %d need more than %zu bytes of LDS", hidden, ffn, kLdsLimit);
+  if (ffn > STRATA_MAX_FFN) return fail(STRATA_EUNSUPPORTED, "ffn %d > %d", ffn, STRATA_MAX_FFN);
   const MoeWs w = moe_ws(rows, hidden, ffn, top_k);
   if (ws_bytes < w.total) return fail(STRATA_EINVAL, "moe workspace %zu < %zu bytes", ws_bytes, w.total);
   const int n_ranges = sw::down_ranges(hidden);

@@ -51,25 +51,41 @@ __device__ __forceinline__ float load_x(const void* x, long i) {
 // 128 + q. The lane's elements then hold the inputs in the order
 //     element e : input k0 + kPerm[e],   kPerm = {0, 4, 1, 5, 2, 6, 3, 7}
 // and the activations staged for the other operand use the same order.
-__device__ __forceinline__ bf16x8 q4_to_bf16x8(uint32_t v) {
+//
+// The masks and the constant are kept in VGPRs (CodeConsts): with three register
+// operands each mask-and-merge is one v_and_or_b32 (VOP3 on gfx9 takes no literal, so
+// with literal constants the compiler emits a separate and + or).
+struct CodeConsts {
+  uint32_t m4, m2, magic;
+};
+
+__device__ __forceinline__ CodeConsts code_consts() {
+  CodeConsts c;
+  asm("v_mov_b32 %0, 0x000f000f" : "=v"(c.m4));
+  asm("v_mov_b32 %0, 0x00030003" : "=v"(c.m2));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(c.magic));
+  return c;
+}
+
+__device__ __forceinline__ bf16x8 q4_to_bf16x8(uint32_t v, const CodeConsts& k) {
   u32x4 w;
-  w[0] = (v & 0x000F000Fu) | 0x43004300u;
-  w[1] = ((v >> 4) & 0x000F000Fu) | 0x43004300u;
-  w[2] = ((v >> 8) & 0x000F000Fu) | 0x43004300u;
-  w[3] = ((v >> 12) & 0x000F000Fu) | 0x43004300u;
+  w[0] = (v & k.m4) | k.magic;
+  w[1] = ((v >> 4) & k.m4) | k.magic;
+  w[2] = ((v >> 8) & k.m4) | k.magic;
+  w[3] = ((v >> 12) & k.m4) | k.magic;
   return __builtin_bit_cast(bf16x8, w);
 }
 
 // 2-bit: the 8 codes of one block are 16 bits (code i at bits 2i). Spreading the two
 // bytes into the two halves of a word gives, per shift 2i, codes i and i+4: the same
 // element order as q4_to_bf16x8.
-__device__ __forceinline__ bf16x8 q2_to_bf16x8(uint32_t half16) {
+__device__ __forceinline__ bf16x8 q2_to_bf16x8(uint32_t half16, const CodeConsts& k) {
   const uint32_t v = (half16 & 0xFFu) | ((half16 & 0xFF00u) << 8);
   u32x4 w;
-  w[0] = (v & 0x00030003u) | 0x43004300u;
-  w[1] = ((v >> 2) & 0x00030003u) | 0x43004300u;
-  w[2] = ((v >> 4) & 0x00030003u) | 0x43004300u;
-  w[3] = ((v >> 6) & 0x00030003u) | 0x43004300u;
+  w[0] = (v & k.m2) | k.magic;
+  w[1] = ((v >> 2) & k.m2) | k.magic;
+  w[2] = ((v >> 4) & k.m2) | k.magic;
+  w[3] = ((v >> 6) & k.m2) | k.magic;
   return __builtin_bit_cast(bf16x8, w);
 }
 
@@ -90,6 +106,84 @@ __device__ __forceinline__ f16x8 q8_to_f16x8(uint32_t lo, uint32_t hi) {
 // Input offset (within 8) held by operand element e.
 __device__ __forceinline__ int perm_q(int e) { return ((e & 1) << 2) | (e >> 1); }   // 0 4 1 5 2 6 3 7
 __device__ __forceinline__ int perm_q8(int e) { return (e & 4) | ((e & 1) << 1) | ((e >> 1) & 1); } // 0 2 1 3 4 6 5 7
+
+// ------------------------------------------------------------ cross-row gathers
+// Lane l = 16*q + c holds v_q (one value per 16-lane row q, for column c). Returns, in
+// every lane of column c, the four values v_0..v_3 (gfx950 permlane swaps: two rows
+// exchange halves, then neighbouring rows).
+__device__ __forceinline__ void gather_rows(uint32_t v, uint32_t (&out)[4]) {
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);      // {r0 r1 r0 r1}, {r2 r3 r2 r3}
+  const auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);  // {r0 x4}, {r1 x4}
+  const auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);  // {r2 x4}, {r3 x4}
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+}
+
+// ------------------------------------------------------------ wave reductions
+// All-reduce over the 64 lanes of a wave without LDS: DPP within rows of 16 (swap
+// neighbours, swap pairs, mirror within 8, mirror within 16), then the gfx950 permlane
+// swaps across rows. Every lane ends with the same value when op is commutative (each
+// step combines two lanes that hold the same pair of operands).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// A value of N 32-bit words, permuted word by word.
+template <int N>
+struct Words {
+  uint32_t w[N];
+};
+
+template <int CTRL, int N>
+__device__ __forceinline__ Words<N> dpp_words(const Words<N>& v) {
+  Words<N> r;
+#pragma unroll
+  for (int i = 0; i < N; i++) r.w[i] = dpp32<CTRL>(v.w[i]);
+  return r;
+}
+
+template <int N, class Op>
+__device__ __forceinline__ Words<N> wave_allreduce_words(Words<N> v, Op op) {
+  v = op(v, dpp_words<0xB1>(v));    // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, dpp_words<0x4E>(v));    // quad_perm [2,3,0,1]: lane ^ 2
+  v = op(v, dpp_words<0x141>(v));   // row_half_mirror: 7 - lane within 8
+  v = op(v, dpp_words<0x140>(v));   // row_mirror: 15 - lane within 16
+  Words<N> a, b;
+#pragma unroll
+  for (int i = 0; i < N; i++) {     // rows {0,1} and {2,3} exchange
+    const auto p = __builtin_amdgcn_permlane16_swap(v.w[i], v.w[i], false, false);
+    a.w[i] = p[0];
+    b.w[i] = p[1];
+  }
+  v = op(a, b);
+#pragma unroll
+  for (int i = 0; i < N; i++) {     // halves exchange
+    const auto p = __builtin_amdgcn_permlane32_swap(v.w[i], v.w[i], false, false);
+    a.w[i] = p[0];
+    b.w[i] = p[1];
+  }
+  return op(a, b);
+}
+
+__device__ __forceinline__ Words<2> words_of(double d) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, d);
+  return Words<2>{{(uint32_t)u, (uint32_t)(u >> 32)}};
+}
+__device__ __forceinline__ double double_of(const Words<2>& v) {
+  return __builtin_bit_cast(double, (uint64_t)v.w[0] | ((uint64_t)v.w[1] << 32));
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+  return double_of(wave_allreduce_words<2>(words_of(x), [](const Words<2>& p, const Words<2>& q) {
+    return words_of(double_of(p) + double_of(q));
+  }));
+}
+
+__device__ __forceinline__ double wave_max(double x) {
+  return double_of(wave_allreduce_words<2>(words_of(x), [](const Words<2>& p, const Words<2>& q) {
+    return words_of(fmax(double_of(p), double_of(q)));
+  }));
+}
 
 // ------------------------------------------------------------------------ MFMA
 // 16x16x32: A lane l = A[l%16][8*(l/16) + e], B lane l = B[8*(l/16) + e][l%16],

@@ -28,6 +28,8 @@ struct GateUpArgs {
   const int32_t* entry_row; const uint8_t* row_mask;
   float* h;                 // [entries][ffn]
   int max_slots;            // capacity of the active array (offsets: max_slots + 1)
+  int split;                // set by the launcher: waves per item (1 or 2), fixed by the
+                            // shapes alone so a row's sums never depend on the window
 };
 
 struct DownArgs {
@@ -72,5 +74,8 @@ int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int head_workgroups(int vocab);
 int down_ranges(int hidden);
+// dynamic LDS of the gate/up and down kernels (the activation image)
+size_t gateup_lds_bytes(int hidden, int x_dtype);
+size_t down_lds_bytes(int ffn);
 
 }  // namespace sw

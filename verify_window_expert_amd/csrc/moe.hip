@@ -24,34 +24,57 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace sw {
 
 constexpr int kThreads = 256;   // 4 waves
-constexpr int kMaxKgPerWave = 4;  // k-groups a wave keeps in flight
 constexpr int kMaxTopk = 8;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxSlots = kMaxRows * kMaxTopk + 1;   // routed experts a window can use + shared
+#ifndef SW_GU_DEPTH
+#define SW_GU_DEPTH 4
+#endif
+constexpr int kGuDepth = SW_GU_DEPTH;                // gate/up: units in flight per wave (ring slots)
+constexpr int kDnDepth = 8;                          // down: units in flight per wave
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), unrolled: ring
+// slots are then compile-time register arrays.
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// ------------------------------------------------------------ activation operand (LDS)
 // LDS image of the activation operand: rows [nrows][stride] of bf16, inputs permuted
-// within each group of 8 as the code conversion orders them, plus block sums Sx
+// within each group of 8 as the code conversion orders them, one all-zero row (read by
+// the lanes of absent columns, so no read is predicated), then the block sums Sx
 // [blocks][16] (zero for absent columns).
 struct ActLds {
   uint16_t* xs;
   float* sx;
-  int stride;  // elements per row
+  int stride;     // elements per row
+  int zero_row;   // index of the zero row
 };
 
 __device__ __forceinline__ ActLds act_lds(uint8_t* smem, int K, int nrows) {
   ActLds l;
   l.stride = K + 8;
+  l.zero_row = nrows;
   l.xs = (uint16_t*)smem;
-  l.sx = (float*)(smem + (size_t)nrows * l.stride * 2);
+  l.sx = (float*)(smem + (size_t)(nrows + 1) * l.stride * 2);
   return l;
 }
 
 __host__ __device__ inline size_t act_lds_bytes(int K, int nrows) {
-  return (size_t)nrows * (K + 8) * 2 + (size_t)(K / 32) * 16 * 4;
+  return (size_t)(nrows + 1) * (K + 8) * 2 + (size_t)(K / 32) * 16 * 4;
 }
+
+size_t gateup_lds_bytes(int hidden, int x_dtype) { return act_lds_bytes(hidden, x_dtype == 0 ? 16 : 8); }
+size_t down_lds_bytes(int ffn) { return act_lds_bytes(ffn, 16); }
 
 // Convert 8 consecutive source values of row j (inputs 8u..8u+7) to bf16 hi (and lo),
 // store them permuted, and add the block sums (4 consecutive lanes = one block).
@@ -86,329 +109,469 @@ __device__ __forceinline__ void stage_group(const ActLds& l, bool ok, int j, int
   }
 }
 
-// Zero the block sums (absent columns must read 0). Call before staging, then barrier.
-__device__ __forceinline__ void clear_sx(const ActLds& l, int K) {
-  for (int i = threadIdx.x; i < (K / 32) * 16; i += kThreads) l.sx[i] = 0.f;
+// Zero what staging does not write: the zero row and the block sums of absent columns
+// (rows >= nrows; the lo half when there is none). Disjoint from stage_group's writes.
+// THREADS is the workgroup size (a constant: reading blockDim costs a load).
+template <int THREADS>
+__device__ __forceinline__ void zero_absent(const ActLds& l, int K, int nrows, bool with_lo) {
+  u32x4* zr = (u32x4*)(l.xs + (size_t)l.zero_row * l.stride);
+  for (int i = threadIdx.x; i < l.stride / 8; i += THREADS) zr[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = threadIdx.x; i < (K / 32) * 16; i += THREADS) {
+    const int col = i & 15;
+    const bool present = col < 8 ? col < nrows : (with_lo && col - 8 < nrows);
+    if (!present) l.sx[i] = 0.f;
+  }
 }
 
-// Stage nsrc rows of K activations (float or bf16) as the A operand, MAXI groups of 8
-// per thread per pass: all global loads of a pass are issued before any is used.
-template <int MAXI, bool F32SRC>
-__device__ __forceinline__ void stage_rows(const ActLds& l, const void* src, int nsrc, int K, bool with_lo) {
-  const int ngrp = K / 8, total = nsrc * ngrp;
-  const int tid = threadIdx.x;
-  for (int pass = 0; pass < total; pass += MAXI * kThreads) {
-    // unconditional loads with the index clamped into range (issue back to back)
-    u32x4 raw[MAXI][F32SRC ? 2 : 1];
+// Group i (of 8 values) of nsrc rows of width K, converted to floats from the loaded
+// words (float source: two 16-byte words; bf16 source: one).
+template <bool F32SRC>
+__device__ __forceinline__ void group_values(const u32x4 (&raw)[F32SRC ? 2 : 1], bool ok, float (&v)[8]) {
 #pragma unroll
-    for (int it = 0; it < MAXI; it++) {
-      const int i = min(pass + it * kThreads + tid, total - 1);
-      const int j = i / ngrp, u = i % ngrp;
-      if (F32SRC) {
-        const u32x4* p = (const u32x4*)((const float*)src + (long)j * K + 8 * u);
-        raw[it][0] = p[0];
-        raw[it][F32SRC ? 1 : 0] = p[1];
-      } else {
-        raw[it][0] = *(const u32x4*)((const uint16_t*)src + (long)j * K + 8 * u);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < MAXI; it++) {
-      const int base = pass + it * kThreads;
-      if (base >= total) break;  // uniform across the workgroup
-      const int i = base + tid;
-      const bool ok = i < total;
-      const int j = ok ? i / ngrp : 0, u = ok ? i % ngrp : 0;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        if (!ok) v[e] = 0.f;
-        else if (F32SRC) {
-          // element into a plain variable first: a bit cast of a vector-element
-          // expression reads the vector's first element
-          const uint32_t w = raw[it][F32SRC ? (e >> 2) : 0][e & 3];
-          v[e] = __uint_as_float(w);
-        }
-        else v[e] = bf16_to_f32((uint16_t)(raw[it][0][e >> 1] >> (16 * (e & 1))));
-      }
-      stage_group(l, ok, j, u, v, with_lo);
+  for (int e = 0; e < 8; e++) {
+    if (!ok) {
+      v[e] = 0.f;
+    } else if constexpr (F32SRC) {
+      // element into a plain variable first: a bit cast of a vector-element
+      // expression reads the vector's first element
+      const uint32_t w = raw[e >> 2][e & 3];
+      v[e] = __uint_as_float(w);
+    } else {
+      v[e] = bf16_to_f32((uint16_t)(raw[0][e >> 1] >> (16 * (e & 1))));
     }
   }
 }
 
-__device__ __forceinline__ bf16x8 act_operand(const ActLds& l, bool col_ok, int c, int blk, int q) {
-  if (!col_ok) return bf16x8{};
-  return *(const bf16x8*)(l.xs + (size_t)c * l.stride + blk * 32 + q * 8);
+template <bool F32SRC>
+__device__ __forceinline__ void load_group(u32x4 (&raw)[F32SRC ? 2 : 1], const void* src, int K, int j, int u) {
+  if constexpr (F32SRC) {
+    const u32x4* p = (const u32x4*)((const float*)src + (long)j * K + 8 * u);
+    raw[0] = p[0];
+    raw[F32SRC ? 1 : 0] = p[1];
+  } else {
+    raw[0] = *(const u32x4*)((const uint16_t*)src + (long)j * K + 8 * u);
+  }
 }
 
-// Weight loads of one k-group of one matrix for this lane (issued, not yet used).
+// Groups tid, tid + threads, ... (XG of them) of nsrc rows, loaded into registers.
+template <int THREADS, int XG, bool F32SRC>
+__device__ __forceinline__ void load_groups(u32x4 (&xr)[XG][F32SRC ? 2 : 1], const void* src, int nsrc, int K) {
+  const int ngrp = K / 8, total = nsrc * ngrp;
+#pragma unroll
+  for (int it = 0; it < XG; it++) {
+    const int i = min(it * THREADS + (int)threadIdx.x, total - 1);
+    load_group<F32SRC>(xr[it], src, K, i / ngrp, i % ngrp);
+  }
+}
+
+template <int THREADS, int XG, bool F32SRC>
+__device__ __forceinline__ void stage_groups(const ActLds& l, const u32x4 (&xr)[XG][F32SRC ? 2 : 1], int nsrc, int K) {
+  const int ngrp = K / 8, total = nsrc * ngrp;
+#pragma unroll
+  for (int it = 0; it < XG; it++) {
+    const int base = it * THREADS;
+    if (base >= total) break;
+    const int i = base + threadIdx.x;
+    const bool ok = i < total;
+    float v[8];
+    group_values<F32SRC>(xr[it], ok, v);
+    stage_group(l, ok, ok ? i / ngrp : 0, ok ? i % ngrp : 0, v, F32SRC);
+  }
+}
+
+// A lane's view of the image: its row (its column c, or the zero row) at its k-offset,
+// and its block-sum column.
+struct ActLane {
+  const uint16_t* row;   // + blk * 32 -> the lane's 8 elements of block blk
+  const float* sx;       // + blk4 * 16 -> Sx of block blk4 + q for column c
+};
+
+__device__ __forceinline__ ActLane act_lane(const ActLds& l, bool col_ok) {
+  const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+  ActLane al;
+  al.row = l.xs + (size_t)(col_ok ? c : l.zero_row) * l.stride + q * 8;
+  al.sx = l.sx + q * 16 + c;
+  return al;
+}
+
+// ---------------------------------------------------------------------------- weights
+// One (matrix, 16-row tile) as two buffer resources: its codes and its metadata from
+// k-group 0 on (the tiled layout of the header: k-group g at g * 1024 code bytes and
+// g * 16 * NB metadata words). A load then takes the lane's fixed offset in a VGPR and
+// the k-group's offset in an SGPR: no per-load address arithmetic on the vector ALU,
+// and the hardware range check keeps every load inside the tile.
+struct TileRsrc {
+  __amdgpu_buffer_rsrc_t codes, meta;
+};
+
+// word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle
+constexpr int kRsrcWord3 = 0x00020000;
+
+// An expert id read at run time, clamped into [0, E] (E = the shared expert), so that
+// a load is always inside the weights even for an unspecified table entry.
+__device__ __forceinline__ int clamp_expert(int e, int E) { return min(max(e, 0), E); }
+
+template <int BITS>
+__device__ __forceinline__ TileRsrc tile_rsrc(const QDev& m, int expert, int E, int tile, int NG) {
+  constexpr int NB = 512 / BITS / 32;
+  const bool shared = expert == E;
+  const uint8_t* c = shared ? m.sh_codes : m.codes + (long)expert * m.stride_codes;
+  const uint8_t* mt = shared ? m.sh_meta : m.meta + (long)expert * m.stride_meta_bytes;
+  const long chunk = (long)tile * NG;
+  TileRsrc r;
+  r.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(c + chunk * 1024), (short)0, NG * 1024, kRsrcWord3);
+  r.meta = __builtin_amdgcn_make_buffer_rsrc((void*)(mt + chunk * 16 * NB * 4), (short)0, NG * 16 * NB * 4, kRsrcWord3);
+  return r;
+}
+
+// Weight loads of one k-group of one matrix for this lane (issued, not yet used): the
+// lane's 16 bytes of codes, and (per 4 blocks) the metadata of block 4h + l/16 of row
+// l%16, one word per lane. mac_kgroup gathers the row's other blocks from the lanes of
+// the same column (gather_rows) instead of loading them four times.
 template <int BITS>
 struct KGroup {
   static constexpr int NB = 512 / BITS / 32;   // blocks per k-group
   u32x4 codes;
-  uint32_t meta[NB];                           // row l%16: (scale | min << 16) per block
-  uint32_t mpart[NB / 4];                      // block 4h + l/16 of row l%16
+  uint32_t meta[NB / 4];
 };
 
 template <int BITS>
-__device__ __forceinline__ void load_kgroup(KGroup<BITS>& kg, const uint8_t* codes, const uint8_t* meta, int NG,
-                                            int tile, int g) {
+__device__ __forceinline__ void load_kgroup(KGroup<BITS>& kg, const TileRsrc& r, int g) {
   constexpr int NB = KGroup<BITS>::NB;
   const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
-  const long chunk = (long)tile * NG + g;
-  kg.codes = *((const u32x4*)codes + chunk * 64 + lane);
-  const uint32_t* mp = (const uint32_t*)meta + (chunk * 16 + c) * NB;
+  kg.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r.codes, lane * 16, g * 1024, 0));
 #pragma unroll
-  for (int b = 0; b < NB; b += 4) {
-    const u32x4 t = *(const u32x4*)(mp + b);
-    kg.meta[b] = t[0]; kg.meta[b + 1] = t[1]; kg.meta[b + 2] = t[2]; kg.meta[b + 3] = t[3];
-  }
-#pragma unroll
-  for (int h = 0; h < NB / 4; h++) kg.mpart[h] = mp[4 * h + q];
+  for (int h = 0; h < NB / 4; h++)
+    kg.meta[h] = __builtin_amdgcn_raw_buffer_load_b32(r.meta, (c * NB + 4 * h + q) * 4, g * 16 * NB * 4, 0);
 }
 
-// Accumulate one k-group of one matrix into acc (C layout: column 4*(l/16)+i, row l%16).
 template <int BITS>
-__device__ __forceinline__ void mac_kgroup(const KGroup<BITS>& kg, const ActLds& l, bool col_ok, int g, f32x4& acc) {
+__device__ __forceinline__ bf16x8 code_operand(const KGroup<BITS>& kg, int beta, const CodeConsts& cc) {
+  return BITS == 4 ? q4_to_bf16x8(kg.codes[beta], cc)
+                   : q2_to_bf16x8((kg.codes[beta >> 1] >> (16 * (beta & 1))) & 0xFFFFu, cc);
+}
+
+// Accumulate one k-group of one matrix (or two matrices against the same activations)
+// into acc (C layout: column 4*(l/16)+i, row l%16).
+template <int BITS, bool TWO>
+__device__ __forceinline__ void mac_kgroup(const KGroup<BITS>& k0, const KGroup<BITS>& k1, const ActLane& al, int g,
+                                           const CodeConsts& cc, f32x4& acc0, f32x4& acc1) {
   constexpr int NB = KGroup<BITS>::NB;
-  const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int beta = 0; beta < NB; beta++) {
-    const bf16x8 ax = act_operand(l, col_ok, c, g * NB + beta, q);
-    const bf16x8 bw = BITS == 4 ? q4_to_bf16x8(kg.codes[beta])
-                                : q2_to_bf16x8((kg.codes[beta >> 1] >> (16 * (beta & 1))) & 0xFFFFu);
-    const f32x4 d = mfma_bf16(ax, bw, z);
-    const float s = f16_lo(kg.meta[beta]);
-#pragma unroll
-    for (int i = 0; i < 4; i++) acc[i] = fmaf(s, d[i], acc[i]);
-  }
-#pragma unroll
   for (int h = 0; h < NB / 4; h++) {
-    const float sx = l.sx[(g * NB + 4 * h + q) * 16 + c];
-    const uint32_t m = kg.mpart[h];
-    acc = mfma_f32x4(sx, f16_hi(m) - 128.f * f16_lo(m), acc);
+    uint32_t m0[4], m1[4];
+    gather_rows(k0.meta[h], m0);
+    if (TWO) gather_rows(k1.meta[h], m1);
+    bf16x8 ax[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) ax[b] = *(const bf16x8*)(al.row + (g * NB + 4 * h + b) * 32);
+    const float sx = al.sx[(g * NB + 4 * h) * 16];
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int beta = 4 * h + b;
+      const f32x4 d0 = mfma_bf16(ax[b], code_operand<BITS>(k0, beta, cc), z);
+      const float s0 = f16_lo(m0[b]);
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc0[i] = fmaf(s0, d0[i], acc0[i]);
+      if (TWO) {
+        const f32x4 d1 = mfma_bf16(ax[b], code_operand<BITS>(k1, beta, cc), z);
+        const float s1 = f16_lo(m1[b]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc1[i] = fmaf(s1, d1[i], acc1[i]);
+      }
+    }
+    // (min - 128 scale) * Sx of blocks 4h..4h+3 by one fp32 MFMA: the lane supplies
+    // block 4h + l/16, exactly the word it loaded
+    acc0 = mfma_f32x4(sx, f16_hi(k0.meta[h]) - 128.f * f16_lo(k0.meta[h]), acc0);
+    if (TWO) acc1 = mfma_f32x4(sx, f16_hi(k1.meta[h]) - 128.f * f16_lo(k1.meta[h]), acc1);
   }
+}
+
+// Units of a wave's work in rounds of DEPTH through the ring (unit u in slot u % DEPTH):
+// full rounds whose refills are all in range, one round whose refills stop at the end,
+// then the remainder. A round has no early exit: an exit inside the round would make the
+// compiler wait for every outstanding load at the loop head.
+template <int DEPTH, class Step>
+__device__ __forceinline__ void run_ring(int units, Step&& step) {
+  int u0 = 0;
+  for (; u0 + 2 * DEPTH <= units; u0 += DEPTH)
+    static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { step(d, true); });
+  if (u0 + DEPTH <= units) {
+    static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { step(d, u0 + d + DEPTH < units); });
+    u0 += DEPTH;
+  }
+  static_for<DEPTH>([&](auto d) __attribute__((always_inline)) {
+    if (u0 + d < units) step(d, false);
+  });
 }
 
 // ------------------------------------------------------------------------ gate / up
-// Persistent: workgroup b takes the items (slot, 16-row ffn tile) b, b + grid, ... of the
-// window's n_active * (ffn / 16) items. It stages the activations once. For every item
-// its 4 waves take the k-groups g = wave, wave + 4, ...; their partial sums meet in LDS
-// in wave order, and wave 0 writes h = silu(gate) * up for the expert's rows.
+// Persistent, one 8-wave workgroup per compute unit. A worker is a group of S waves of
+// one workgroup (S = 2 when the k-groups split evenly and LDS holds the partial sums,
+// else 1: a choice made from the shapes alone, so that a row's arithmetic is the same
+// in every window); it owns whole items (slot, 16-row ffn tile), and wave p of the group streams k-groups
+// [p NG/S, (p+1) NG/S) of the item's gate and up rows through the ring. With S = 2 the
+// two partial sums meet in LDS and the second wave to arrive adds them in part order
+// (so the result does not depend on which arrives first) and writes h. Items go to
+// groups wave-major (item i: workgroup i % grid) so every compute unit gets a share.
+//
+// Start-up: the activations, the routing tables and (by wave-uniform scalar loads) the
+// experts of each wave's first items are loaded in one round and staged in LDS before
+// the first ring of weight units is requested.
 
-template <int BITS>
-__global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) {
+constexpr int kGuWaves = 8, kGuThreads = 64 * kGuWaves;
+constexpr size_t kPartBytes = (size_t)kGuWaves * 2 * 32 * 8 * 4;   // [wave][parity][lane < 32][8]
+
+size_t gateup_split_lds_bytes(int hidden, int x_dtype) { return gateup_lds_bytes(hidden, x_dtype) + kPartBytes; }
+
+// s_waitcnt lgkmcnt(0) that the compiler does not move memory operations across
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int BITS, bool F32IN, int XG>
+__global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
+  constexpr int DEPTH = kGuDepth;
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ f32x4 red[4][2][64];
   __shared__ int s_active[kMaxSlots];
   __shared__ int s_off[kMaxSlots + 1];
   __shared__ uint8_t s_mask[kMaxExperts + 4];
+  __shared__ int s_cnt[kGuWaves][2], s_done[kGuWaves][2];   // per group and item parity
   const int H = a.hidden, F = a.ffn, R = a.rows, E = a.n_experts;
   const int tiles = F / 16;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool f32in = a.x_dtype == 0;
+  // the wave index via readfirstlane: the compiler then knows it (and every count
+  // derived from it) is uniform in the wave, and keeps the pipeline's control scalar
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   constexpr int G = 512 / BITS;
   const int NG = H / G;
+  const int grid = gridDim.x;
 
-  // round 1: the first item's expert, the active count and every routing table, all at
-  // once (clamped loads; the arrays hold max_slots, max_slots + 1 and E + 1 entries)
-  int it = blockIdx.x;
-  const int n_active = *a.n_active;
-  int e = a.active[it / tiles];
+  // the activations (XG groups of 8 per thread) and the tables, all loads at once
+  const ActLds l = act_lds(smem, H, F32IN ? 16 : 8);
+  float* const s_part = (float*)(smem + act_lds_bytes(H, F32IN ? 16 : 8));   // k-split partials
+  u32x4 xr[XG][F32IN ? 2 : 1];
+  load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
   const int sa = a.active[min(tid, a.max_slots - 1)];
   const int so = a.offsets[min(tid, a.max_slots)];
-  const uint8_t sm = a.row_mask[min(tid, E)], sm2 = a.row_mask[min(tid + kThreads, E)];
-  const int items = n_active * tiles;
-  if (it >= items) return;
+  const uint8_t sm = a.row_mask[min(tid, E)];
+  __builtin_amdgcn_sched_barrier(0);
 
-  // round 2: the first item's weights (this wave's k-groups, clamped loads)
-  KGroup<BITS> kgg[kMaxKgPerWave], kgu[kMaxKgPerWave];
-  auto mats = [&](int expert, const uint8_t*& gc, const uint8_t*& gm, const uint8_t*& uc, const uint8_t*& um) {
-    const bool shared = expert == E;
-    gc = shared ? a.gate.sh_codes : a.gate.codes + expert * a.gate.stride_codes;
-    gm = shared ? a.gate.sh_meta : a.gate.meta + expert * a.gate.stride_meta_bytes;
-    uc = shared ? a.up.sh_codes : a.up.codes + expert * a.up.stride_codes;
-    um = shared ? a.up.sh_meta : a.up.meta + expert * a.up.stride_meta_bytes;
+  // the active count: a wave-uniform scalar load in the same round
+  const int n_active = __builtin_amdgcn_readfirstlane(*a.n_active);
+  const int S = a.split;
+  const int gw = kGuWaves / S;                     // groups per workgroup
+  const int part = wave / gw, gl = wave % gw;      // part of the k-range; group in the workgroup
+  const int Wg = grid * gw;                        // groups
+  const int me = gl * grid + blockIdx.x;           // this wave's group
+  const int NGs = NG / S;                          // k-groups per part
+  const int items = n_active * tiles;
+  const int my_items = me < items ? (items - me + Wg - 1) / Wg : 0;
+  const int units = my_items * NGs;
+
+  // issue side of the ring: the next unit is k-group part * NGs + is_g of item ordinal
+  // is_j, whose tiles are rg / ru; past the last item it stays on the last one
+  KGroup<BITS> kgg[DEPTH], kgu[DEPTH];
+  int is_j = 0, is_g = 0;
+  TileRsrc rg, ru;
+  auto set_item = [&](int expert, int j) __attribute__((always_inline)) {
+    const int tile = (me + j * Wg) % tiles;
+    expert = clamp_expert(expert, E);
+    rg = tile_rsrc<BITS>(a.gate, expert, E, tile, NG);
+    ru = tile_rsrc<BITS>(a.up, expert, E, tile, NG);
   };
-  {
-    const uint8_t *gc, *gm, *uc, *um;
-    mats(e, gc, gm, uc, um);
-#pragma unroll
-    for (int i = 0; i < kMaxKgPerWave; i++) {
-      const int g = min(wave + 4 * i, NG - 1);
-      load_kgroup<BITS>(kgg[i], gc, gm, NG, it % tiles, g);
-      load_kgroup<BITS>(kgu[i], uc, um, NG, it % tiles, g);
+  auto issue_next = [&](auto d_, auto&& expert_of) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_)::value;
+    load_kgroup<BITS>(kgg[d], rg, part * NGs + is_g);
+    load_kgroup<BITS>(kgu[d], ru, part * NGs + is_g);
+    if (++is_g == NGs) {
+      is_g = 0;
+      if (is_j + 1 < my_items) {
+        ++is_j;
+        set_item(expert_of(is_j), is_j);
+      }
     }
-  }
+  };
+  // The activation image, the tables and the split counters go into LDS before any
+  // weight is requested: the prologue's loads then meet an idle memory system (behind
+  // other waves' weight streams they would take several times as long, and the
+  // barrier waits for the slowest wave of the workgroup).
   if (tid < a.max_slots) s_active[tid] = sa;
   if (tid <= a.max_slots) s_off[tid] = so;
   if (tid <= E) s_mask[tid] = sm;
-  if (tid + kThreads <= E) s_mask[tid + kThreads] = sm2;
-
-  // activations (L2-resident), staged while the weights stream in
-  const ActLds l = act_lds(smem, H, f32in ? 16 : 8);
-  clear_sx(l, H);
+  if (tid < kGuWaves * 2) { (&s_cnt[0][0])[tid] = 0; (&s_done[0][0])[tid] = 0; }
+  zero_absent<kGuThreads>(l, H, R, F32IN);
+  stage_groups<kGuThreads, XG, F32IN>(l, xr, R, H);   // the launcher picks XG to cover all groups
   __syncthreads();
-  if (f32in) stage_rows<4, true>(l, a.x, R, H, true);
-  else stage_rows<8, false>(l, a.x, R, H, false);
-  __syncthreads();
+  if (units == 0) return;
+  // the expert of item ordinal j (the table in LDS)
+  auto lds_of = [&](int j) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(s_active[min((me + j * Wg) / tiles, kMaxSlots - 1)]);
+  };
+  set_item(lds_of(0), 0);
+  static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { issue_next(d, lds_of); });
 
   const int c = lane & 15, q = lane >> 4;
-  const bool col_ok = (c & 7) < R && (c < 8 || f32in);
-  for (;;) {
-    const int slot = it / tiles, tile = it % tiles;
-    const int next = it + gridDim.x;
-    const bool more = next < items;
-    const int e_next = s_active[min(next, items - 1) / tiles];
-    const uint8_t *ngc, *ngm, *nuc, *num;
-    mats(e_next, ngc, ngm, nuc, num);
-    f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-    // consume each k-group, then refill its registers with the next item's
+  const ActLane al = act_lane(l, (c & 7) < R && (c < 8 || F32IN));
+  const CodeConsts cc = code_consts();
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+  int cu_j = 0, cu_g = 0;
+  // h = silu(gate) * up for the item's rows, from the finished sums (lanes < 32)
+  auto write_h = [&](const f32x4& gs, const f32x4& us) __attribute__((always_inline)) {
+    const int item = me + cu_j * Wg;
+    const int slot = item / tiles, tile = item % tiles, e = s_active[slot];
+    const uint32_t rmask = s_mask[e];
+    const int ent0 = s_off[slot];
 #pragma unroll
-    for (int i = 0; i < kMaxKgPerWave; i++) {
-      const int g = wave + 4 * i;
-      if (g < NG) {
-        mac_kgroup<BITS>(kgg[i], l, col_ok, g, ag);
-        mac_kgroup<BITS>(kgu[i], l, col_ok, g, au);
-      }
-      if (more) {
-        const int gn = min(g, NG - 1);
-        load_kgroup<BITS>(kgg[i], ngc, ngm, NG, next % tiles, gn);
-        load_kgroup<BITS>(kgu[i], nuc, num, NG, next % tiles, gn);
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * q + i;
+      if (r < R && ((rmask >> r) & 1u)) {
+        const int ent = ent0 + __builtin_popcount(rmask & ((1u << r) - 1u));
+        const float gv = gs[i];
+        a.h[(long)ent * F + tile * 16 + c] = gv / (1.f + expf(-gv)) * us[i];
       }
     }
-    // k-groups beyond 4 per wave (wider hidden): streamed, same order
-    if (NG > 4 * kMaxKgPerWave) {
-      const uint8_t *gc, *gm, *uc, *um;
-      mats(e, gc, gm, uc, um);
-      for (int g = wave + 4 * kMaxKgPerWave; g < NG; g += 4) {
-        KGroup<BITS> tg, tu;
-        load_kgroup<BITS>(tg, gc, gm, NG, tile, g);
-        load_kgroup<BITS>(tu, uc, um, NG, tile, g);
-        mac_kgroup<BITS>(tg, l, col_ok, g, ag);
-        mac_kgroup<BITS>(tu, l, col_ok, g, au);
-      }
-    }
-
-    red[wave][0][lane] = ag;
-    red[wave][1][lane] = au;
-    __syncthreads();
-    if (wave == 0) {
-      ag = red[0][0][lane]; au = red[0][1][lane];
+  };
+  // after this wave's last k-group of an item
+  auto finish_item = [&]() __attribute__((always_inline)) {
+    if constexpr (F32IN) {
 #pragma unroll
-      for (int w = 1; w < 4; w++) {
-        const f32x4 tg = red[w][0][lane], tu = red[w][1][lane];
-#pragma unroll
-        for (int i = 0; i < 4; i++) { ag[i] += tg[i]; au[i] += tu[i]; }
-      }
-      // hi column r (lanes 0..31) + lo column 8 + r (lanes 32..63)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < 4; i++) {   // hi column r (lanes 0..31) + lo column 8 + r
         ag[i] += __shfl_down(ag[i], 32);
         au[i] += __shfl_down(au[i], 32);
       }
+    }   // (bf16 x: the lo columns read the zero row and hold exact zeros)
+    if (S == 1) {
+      if (lane < 32) write_h(ag, au);
+    } else {
+      const int par = cu_j & 1;
+      // the buffers of this parity were last used by item cu_j - 2: wait until its
+      // last arriver has read them
+      // (relaxed atomic loads: a volatile one would make the compiler wait for every
+      // outstanding weight load as well)
+      if (cu_j >= 2)
+        while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&s_done[gl][par], __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_WORKGROUP)) < cu_j - 1) {}
+      float* mine = s_part + ((size_t)(wave * 2 + par) * 32 + lane) * 8;
       if (lane < 32) {
-        const uint32_t rmask = s_mask[e];
-        const int ent0 = s_off[slot];
+        *(f32x4*)mine = ag;
+        *(f32x4*)(mine + 4) = au;
+      }
+      lds_wait();   // the partial is in LDS before the arrival is counted
+      int old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(&s_cnt[gl][par], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __builtin_amdgcn_readfirstlane(old);
+      asm volatile("" ::: "memory");   // no LDS read is hoisted above the arrival
+      if (old % 2 == 1) {   // second to arrive: part 0 + part 1, in that order
+        if (lane < 32) {
+          const float* p0 = s_part + ((size_t)(gl * 2 + par) * 32 + lane) * 8;          // wave gl: part 0
+          const float* p1 = s_part + ((size_t)((gw + gl) * 2 + par) * 32 + lane) * 8;   // wave gw + gl: part 1
+          const f32x4 g0 = *(const f32x4*)p0, u0 = *(const f32x4*)(p0 + 4);
+          const f32x4 g1 = *(const f32x4*)p1, u1 = *(const f32x4*)(p1 + 4);
+          f32x4 gs, us;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int r = 4 * q + i;
-          if (r < R && ((rmask >> r) & 1u)) {
-            const int ent = ent0 + __builtin_popcount(rmask & ((1u << r) - 1u));
-            const float g = ag[i];
-            a.h[(long)ent * F + tile * 16 + c] = g / (1.f + expf(-g)) * au[i];
+          for (int i = 0; i < 4; i++) {
+            gs[i] = g0[i] + g1[i];
+            us[i] = u0[i] + u1[i];
           }
+          write_h(gs, us);
         }
+        lds_wait();   // both partials are read before the buffers are released
+        if (lane == 0) __hip_atomic_store(&s_done[gl][par], cu_j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
-    if (!more) break;
-    __syncthreads();   // red is reused by the next item
-    it = next;
-    e = e_next;
-  }
+    ag = f32x4{0.f, 0.f, 0.f, 0.f};
+    au = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  run_ring<DEPTH>(units, [&](auto d_, bool refill) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_)::value;
+    mac_kgroup<BITS, true>(kgg[d], kgu[d], al, part * NGs + cu_g, cc, ag, au);
+    if (refill) issue_next(d_, lds_of);
+    if (++cu_g == NGs) {
+      finish_item();
+      cu_g = 0;
+      ++cu_j;
+    }
+  });
 }
 
 // --------------------------------------------------------------------------- down
-// Persistent: workgroup b takes the items (slot, 64 output rows) b, b + grid, ...; for
-// an item wave w owns the 16-row tile w and all ffn inputs. y[entry][row] is written
-// for each of the expert's rows; k_combine sums them.
+// Persistent, 8-wave workgroups; workgroup b serves expert slot b % n_active (the
+// workgroups of a slot split its output tiles) and stages that expert's h once; each
+// wave streams whole 16-row output tiles through the ring. y[entry][row] is written for
+// each of the expert's rows; k_combine sums them. As in gate/up, h (from L2) is staged
+// in LDS before the weights are requested.
 
-constexpr int kDownRange = 64;
+constexpr int kDnWaves = 8, kDnThreads = 64 * kDnWaves;
+constexpr int kDownRange = 64;   // rows per combine workgroup
 
-template <int BITS>
-__global__ __launch_bounds__(kThreads) void k_down(DownArgs a) {
+template <int BITS, int XG>
+__global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
+  constexpr int DEPTH = kDnDepth;
   extern __shared__ __align__(16) uint8_t smem[];
   const int H = a.hidden, F = a.ffn, E = a.n_experts;
-  const int NR = a.n_ranges;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   constexpr int G = 512 / BITS;
   const int NG = F / G;
-  constexpr int KMAX = 8;                 // ffn up to 8 k-groups held in flight
   const int tiles_h = H / 16;
 
-  // round 1: the first item's routing
-  int it = blockIdx.x;
-  const int n_active = *a.n_active;
-  int slot = it / NR;
-  int e = a.active[slot];
-  int e0 = a.offsets[slot], e1 = a.offsets[slot + 1];
-  const int items = n_active * NR;
-  if (it >= items) return;
-
-  auto mats = [&](int expert, const uint8_t*& dc, const uint8_t*& dm) {
-    const bool shared = expert == E;
-    dc = shared ? a.down.sh_codes : a.down.codes + expert * a.down.stride_codes;
-    dm = shared ? a.down.sh_meta : a.down.meta + expert * a.down.stride_meta_bytes;
+  // one round: the active count (scalar) and the slot tables (lane i: slots i, 64 + i)
+  const int ms = a.max_slots;
+  const int act0 = a.active[min(lane, ms - 1)], act1 = a.active[min(64 + lane, ms - 1)];
+  const int off0 = a.offsets[min(lane, ms)], off1 = a.offsets[min(64 + lane, ms)];
+  const int n_active = __builtin_amdgcn_readfirstlane(*a.n_active);
+  const int slot = blockIdx.x % n_active;
+  auto pick = [&](int v0, int v1, int i) __attribute__((always_inline)) {
+    return i < 64 ? __builtin_amdgcn_readlane(v0, i) : __builtin_amdgcn_readlane(v1, i - 64);
   };
-  // round 2: the first item's weights (clamped loads: unused copies of the last
-  // k-group / tile)
-  KGroup<BITS> kg[KMAX];
-  {
-    const uint8_t *dc, *dm;
-    mats(e, dc, dm);
-    const int tile = min((it % NR) * 4 + wave, tiles_h - 1);
-#pragma unroll
-    for (int i = 0; i < KMAX; i++) load_kgroup<BITS>(kg[i], dc, dm, NG, tile, min(i, NG - 1));
-  }
+  const int e = clamp_expert(pick(act0, act1, slot), E);
+  const int e0 = pick(off0, off1, slot), ne = pick(off0, off1, slot + 1) - e0;
+  // workgroups of this slot: b = slot + k * n_active, k < nw
+  const int k = blockIdx.x / n_active;
+  const int nw = (gridDim.x - slot + n_active - 1) / n_active;
+  // this wave's tiles: t = k * 8 + wave + j * (nw * 8)
+  const int stride = nw * kDnWaves, t0 = k * kDnWaves + wave;
+  const int my_tiles = t0 < tiles_h ? (tiles_h - t0 + stride - 1) / stride : 0;
+  const int units = my_tiles * NG;
 
+  // the expert's h (XG groups of 8 per thread)
   const ActLds l = act_lds(smem, F, 16);
-  const int c = lane & 15, q = lane >> 4;
-  for (;;) {
-    const int nr = it % NR;
-    const int tile = nr * 4 + wave;
-    const bool has_tile = tile * 16 < H;
-    const int ne = e1 - e0;
-    clear_sx(l, F);
-    __syncthreads();
-    stage_rows<4, true>(l, a.h + (long)e0 * F, ne, F, true);
-    // the next item's routing, read while this one computes
-    const int next = it + gridDim.x;
-    const bool more = next < items;
-    const int nslot = min(next, items - 1) / NR;
-    const int ne_e = a.active[nslot], ne0 = a.offsets[nslot], ne1 = a.offsets[nslot + 1];
-    __syncthreads();
-    const uint8_t *ndc, *ndm;
-    mats(ne_e, ndc, ndm);
-    const int ntile = min((next % NR) * 4 + wave, tiles_h - 1);
-    const bool col_ok = (c & 7) < ne;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // consume each k-group, then refill its registers with the next item's
-#pragma unroll
-    for (int i = 0; i < KMAX; i++) {
-      if (has_tile && i < NG) mac_kgroup<BITS>(kg[i], l, col_ok, i, acc);
-      if (more) load_kgroup<BITS>(kg[i], ndc, ndm, NG, ntile, min(i, NG - 1));
-    }
-    if (has_tile) {
-      if (NG > KMAX) {
-        const uint8_t *dc, *dm;
-        mats(e, dc, dm);
-        for (int g = KMAX; g < NG; g++) {
-          KGroup<BITS> t;
-          load_kgroup<BITS>(t, dc, dm, NG, tile, g);
-          mac_kgroup<BITS>(t, l, col_ok, g, acc);
-        }
+  const float* hsrc = a.h + (long)e0 * F;
+  u32x4 hr[XG][2];
+  load_groups<kDnThreads, XG, true>(hr, hsrc, max(ne, 1), F);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // h into LDS before any weight is requested (as in gate/up)
+  zero_absent<kDnThreads>(l, F, ne, true);
+  stage_groups<kDnThreads, XG, true>(l, hr, ne, F);   // the launcher picks XG to cover all groups
+  __syncthreads();
+  if (units == 0) return;
+
+  KGroup<BITS> kg[DEPTH];
+  int is_j = 0, is_g = 0;
+  TileRsrc pd = tile_rsrc<BITS>(a.down, e, E, t0, NG);
+  auto issue_next = [&](auto d_) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_)::value;
+    load_kgroup<BITS>(kg[d], pd, is_g);
+    if (++is_g == NG) {
+      is_g = 0;
+      if (is_j + 1 < my_tiles) {
+        ++is_j;
+        pd = tile_rsrc<BITS>(a.down, e, E, t0 + is_j * stride, NG);
       }
+    }
+  };
+  static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { issue_next(d); });
+
+  const int c = lane & 15, q = lane >> 4;
+  const ActLane al = act_lane(l, (c & 7) < ne);
+  const CodeConsts cc = code_consts();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int cu_j = 0, cu_g = 0;
+  run_ring<DEPTH>(units, [&](auto d_, bool refill) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_)::value;
+    mac_kgroup<BITS, false>(kg[d], kg[d], al, cu_g, cc, acc, acc);
+    if (refill) issue_next(d_);
+    if (++cu_g == NG) {
+      const int tile = t0 + cu_j * stride;
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[i] += __shfl_down(acc[i], 32);
       if (lane < 32) {
@@ -418,11 +581,11 @@ __global__ __launch_bounds__(kThreads) void k_down(DownArgs a) {
           if (j < ne) a.y[(long)(e0 + j) * H + tile * 16 + c] = acc[i];
         }
       }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      cu_g = 0;
+      ++cu_j;
     }
-    if (!more) break;
-    __syncthreads();   // the staged h is replaced by the next item's
-    it = next; slot = nslot; e = ne_e; e0 = ne0; e1 = ne1;
-  }
+  });
 }
 
 // ------------------------------------------------------------------------ combine
@@ -503,64 +666,115 @@ __global__ __launch_bounds__(kThreads) void k_combine(DownArgs a) {
 
 // ------------------------------------------------------------------------ launchers
 
-// Raise a kernel's dynamic LDS limit above the default 64 KB (once per process and
-// kernel; the attribute only grows, so a later smaller launch needs nothing).
-template <auto kernel>
-static int set_lds(size_t bytes) {
-  static size_t granted = 64 * 1024;
-  if (bytes <= granted) return 0;
-  const int e = (int)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == 0) granted = bytes;
-  return e;
-}
 
-// Persistent grids: as many workgroups as can be resident at once (occupancy of the
-// kernel at this LDS size, per compute unit, times the compute units), never more than
-// the window can use. Cached per kernel and LDS size.
-template <auto kernel>
-static int persistent_grid(size_t lds, int max_items) {
-  static size_t cached_lds = 0;
-  static int resident = 0;
-  if (!resident || cached_lds != lds) {
-    int dev = 0, cus = 0, per_cu = 0;
+// Persistent grids: resident workgroups per compute unit (occupancy of the kernel at
+// this block and LDS size, capped by per_cu_max) times the compute units, never more
+// than the window can use. Cached per kernel and LDS size.
+static int compute_units() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess || per_cu <= 0)
+  }
+  return cus;
+}
+
+template <auto kernel>
+static int persistent_grid(int threads, size_t lds, int max_items, int per_cu_max) {
+  static size_t cached_lds = 0;
+  static int resident = 0;
+  if (!resident || cached_lds != lds) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
       per_cu = 1;
-    resident = cus * per_cu;
+    resident = compute_units() * (per_cu < per_cu_max ? per_cu : per_cu_max);
     cached_lds = lds;
   }
   return max_items < resident ? max_items : resident;
 }
 
-int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p) {
-  const size_t lds = act_lds_bytes(a.hidden, a.x_dtype == 0 ? 16 : 8);
-  const int items = max_slots * (a.ffn / 16);
-  if (a.bits == 4) {
-    if (int e = set_lds<k_gateup<4>>(lds)) return e;
-    launch(k_gateup<4>, dim3(persistent_grid<k_gateup<4>>(lds, items)), dim3(kThreads), lds, s, p, a);
-  } else {
-    if (int e = set_lds<k_gateup<2>>(lds)) return e;
-    launch(k_gateup<2>, dim3(persistent_grid<k_gateup<2>>(lds, items)), dim3(kThreads), lds, s, p, a);
+// Raise a kernel's dynamic LDS limit when static + dynamic exceed the default 64 KB (once
+// per process and kernel; the attribute only grows).
+template <auto kernel>
+static int set_lds(size_t bytes) {
+  static size_t granted = 0;
+  if (bytes <= granted) return 0;
+  hipFuncAttributes fa;
+  if (int e = (int)hipFuncGetAttributes(&fa, (const void*)kernel)) return e;
+  if (fa.sharedSizeBytes + bytes > 64 * 1024) {
+    const int e = (int)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e) return e;
   }
-  return (int)hipGetLastError();
+  granted = bytes;
+  return 0;
+}
+
+template <int BITS, bool F32IN, int XG>
+static int launch_gateup_k(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
+  if (int e = set_lds<k_gateup<BITS, F32IN, XG>>(lds)) return e;
+  launch(k_gateup<BITS, F32IN, XG>, dim3(persistent_grid<k_gateup<BITS, F32IN, XG>>(kGuThreads, lds, items, 1)),
+         dim3(kGuThreads), lds, s, p, a);
+  return 0;
+}
+
+template <int BITS, bool F32IN>
+static int launch_gateup_x(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
+  // activation groups of 8 per thread, all loaded up front (rows * hidden / 8 <= 16 * 512
+  // for every hidden whose image fits in LDS)
+  const int groups = a.rows * (a.hidden / 8);
+  if (groups <= 4 * kGuThreads) return launch_gateup_k<BITS, F32IN, 4>(a, lds, items, s, p);
+  if (groups <= 8 * kGuThreads) return launch_gateup_k<BITS, F32IN, 8>(a, lds, items, s, p);
+  if (groups <= 16 * kGuThreads) return launch_gateup_k<BITS, F32IN, 16>(a, lds, items, s, p);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_gateup(const GateUpArgs& a0, int max_slots, hipStream_t s, const Prof* p) {
+  GateUpArgs a = a0;
+  const bool f32 = a.x_dtype == 0;
+  // two waves per item when the k-groups split evenly and the partial-sum buffers fit
+  // next to the activation image
+  const int NG = a.hidden / (512 / a.bits);
+  a.split = (NG % 2 == 0 && gateup_split_lds_bytes(a.hidden, a.x_dtype) + 2048 <= 160 * 1024) ? 2 : 1;
+  const size_t lds = a.split == 2 ? gateup_split_lds_bytes(a.hidden, a.x_dtype) : gateup_lds_bytes(a.hidden, a.x_dtype);
+  const int items = max_slots * (a.ffn / 16);
+  int e;
+  if (a.bits == 4)
+    e = f32 ? launch_gateup_x<4, true>(a, lds, items, s, p) : launch_gateup_x<4, false>(a, lds, items, s, p);
+  else
+    e = f32 ? launch_gateup_x<2, true>(a, lds, items, s, p) : launch_gateup_x<2, false>(a, lds, items, s, p);
+  return e ? e : (int)hipGetLastError();
 }
 
 int down_ranges(int hidden) { return (hidden + kDownRange - 1) / kDownRange; }
 
+template <int BITS, int XG>
+static int launch_down_k(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
+  if (int e = set_lds<k_down<BITS, XG>>(lds)) return e;
+  // at least one workgroup per slot, so that every expert is served
+  int grid = persistent_grid<k_down<BITS, XG>>(kDnThreads, lds, 1 << 30, 1);
+  if (grid < max_slots) grid = max_slots;
+  launch(k_down<BITS, XG>, dim3(grid), dim3(kDnThreads), lds, s, p, a);
+  return 0;
+}
+
+template <int BITS>
+static int launch_down_bits(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
+  // h groups (8 floats) of up to 8 rows per thread, all loaded up front (8 * ffn / 8)
+  if (a.ffn <= 2 * kDnThreads) return launch_down_k<BITS, 2>(a, lds, max_slots, s, p);
+  if (a.ffn <= 4 * kDnThreads) return launch_down_k<BITS, 4>(a, lds, max_slots, s, p);
+  if (a.ffn <= 8 * kDnThreads) return launch_down_k<BITS, 8>(a, lds, max_slots, s, p);
+  return (int)hipErrorInvalidValue;
+}
+
 int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p) {
-  const size_t lds = act_lds_bytes(a.ffn, 16);
-  const int items = max_slots * a.n_ranges;
+  const size_t lds = down_lds_bytes(a.ffn);
   Prof p0, p1;
   if (p) { p0.start = p->start; p1.stop = p->stop; }
-  if (a.bits == 4) {
-    if (int e = set_lds<k_down<4>>(lds)) return e;
-    launch(k_down<4>, dim3(persistent_grid<k_down<4>>(lds, items)), dim3(kThreads), lds, s, p ? &p0 : nullptr, a);
-  } else {
-    if (int e = set_lds<k_down<2>>(lds)) return e;
-    launch(k_down<2>, dim3(persistent_grid<k_down<2>>(lds, items)), dim3(kThreads), lds, s, p ? &p0 : nullptr, a);
-  }
+  const int e = a.bits == 4 ? launch_down_bits<4>(a, lds, max_slots, s, p ? &p0 : nullptr)
+                            : launch_down_bits<2>(a, lds, max_slots, s, p ? &p0 : nullptr);
+  if (e) return e;
   if (a.x_dtype == 0)
     launch(k_combine<true>, dim3(a.n_ranges), dim3(kThreads), 0, s, p ? &p1 : nullptr, a);
   else

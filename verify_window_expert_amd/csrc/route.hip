@@ -10,6 +10,7 @@
 // k_route_final (one workgroup) adds the partials in chunk order, then runs softmax,
 // top-k and grouping for the whole window. (A completion ticket in one launch would
 // serialise one device-scope atomic per workgroup, which costs more than the launch.)
+// Reductions inside a wave use DPP and the permlane swaps (common.h), not LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,12 +18,7 @@ namespace sw {
 
 constexpr int kRouteChunk = 512;          // inputs per workgroup
 constexpr int kRouteWaves = 4;            // experts per workgroup
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
+constexpr int kMaxExpertsRoute = 256;     // the ABI's limit on experts
 
 template <bool F32IN>
 __global__ __launch_bounds__(256) void k_route_logits(RouteArgs a) {
@@ -79,7 +75,7 @@ __global__ __launch_bounds__(256) void k_route_logits(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < kMaxRows; r++) {
       if (r >= R) break;
-      const double s = wave_sum_d(acc[r]);
+      const double s = wave_sum(acc[r]);
       if (lane == 0) a.partials[((long)hc * R + r) * E + e] = s;
     }
   }
@@ -90,172 +86,155 @@ __device__ __forceinline__ bool better(double l, int e, double lb, int eb) {
   return l > lb || (l == lb && e < eb);
 }
 
+// (logit, expert) of the wave's best candidate, in every lane.
+__device__ __forceinline__ void wave_argmax(double& l, int& e) {
+  Words<3> v{{(uint32_t)__builtin_bit_cast(uint64_t, l), (uint32_t)(__builtin_bit_cast(uint64_t, l) >> 32),
+              (uint32_t)e}};
+  v = wave_allreduce_words<3>(v, [](const Words<3>& p, const Words<3>& q) {
+    const double lp = double_of(Words<2>{{p.w[0], p.w[1]}}), lq = double_of(Words<2>{{q.w[0], q.w[1]}});
+    return better(lq, (int)q.w[2], lp, (int)p.w[2]) ? q : p;
+  });
+  l = double_of(Words<2>{{v.w[0], v.w[1]}});
+  e = (int)v.w[2];
+}
+
+// popcount of the bits of m held by the lanes below this one
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
 constexpr int kFinalThreads = 512;   // one wave per window row
 
+// One workgroup: wave r adds row r's partials in chunk order, then softmax and top-k for
+// the row (every reduction inside the wave, without LDS); the row's selections go to LDS
+// as a row mask per expert and a weight per (row, expert); waves 0..3 then list the used
+// experts in ascending order with their rows (ballots give every position directly).
 __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
-  __shared__ double lgs[kMaxRows * 256];         // logits [R][E]
-  __shared__ __align__(16) int s_idx[kMaxRows * 8];
-  __shared__ float s_w[kMaxRows * 8];
-  __shared__ uint32_t s_mask[257];
-  __shared__ int s_wsum[2][4];
+  __shared__ uint32_t s_mask[kMaxExpertsRoute + 1];
+  __shared__ float s_wt[kMaxRows][kMaxExpertsRoute];
+  __shared__ int s_tot[2][4];
   const int H = a.hidden, E = a.n_experts, R = a.rows, K = a.top_k;
   const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid < kMaxRows * 8) s_idx[tid] = -1;    // entries past R*K never match an expert
-
-  // logits: every (row, expert) pair's partials (layout [chunk][row][expert]) are read
-  // with unconditional, clamped loads issued together, summed in chunk order, biased
-  {
-    constexpr int MP = kMaxRows * 256 / kFinalThreads, MC = 8;
-    const int RE = R * E;
-    double part[MP][MC];
-    float bias[MP];
-    const float* bp = a.bias ? a.bias : a.gate_w;   // any readable array when unbiased
-#pragma unroll
-    for (int i = 0; i < MP; i++) {
-      const int p = min(i * kFinalThreads + tid, RE - 1);
-#pragma unroll
-      for (int c = 0; c < MC; c++) part[i][c] = a.partials[(long)min(c, n_hc - 1) * RE + p];
-      bias[i] = bp[p % E];
-    }
-#pragma unroll
-    for (int i = 0; i < MP; i++) {
-      const int p = i * kFinalThreads + tid;
-      if (p >= RE) break;
-      double s = 0.0;
-#pragma unroll
-      for (int c = 0; c < MC; c++)
-        if (c < n_hc) s += part[i][c];
-      for (int c = MC; c < n_hc; c++) s += a.partials[(long)c * RE + p];   // hidden > 4096
-      lgs[p] = s + (a.bias ? (double)bias[i] : 0.0);
-    }
-  }
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  for (int i = tid; i <= E; i += kFinalThreads) s_mask[i] = 0u;
   __syncthreads();
 
-  // softmax and top-k of row r = wave; lane holds experts lane + 64u, kept sorted by the
-  // selection key so that each round compares only the lanes' heads
   if (wave < R) {
     const int r = wave;
-    double l[4];
-    int id[4];
+    // logits of experts lane + 64u: every chunk's partial loaded at once (clamped,
+    // unconditional), added in chunk order, then the bias
+    constexpr int MU = kMaxExpertsRoute / kWave, MC = 8;
+    double part[MU][MC];
+    float bias[MU];
+    const float* bp = a.bias ? a.bias : a.gate_w;   // any readable array when unbiased
+#pragma unroll
+    for (int u = 0; u < MU; u++) {
+      const int ee = min(u * kWave + lane, E - 1);
+#pragma unroll
+      for (int c = 0; c < MC; c++) part[u][c] = a.partials[((long)min(c, n_hc - 1) * R + r) * E + ee];
+      bias[u] = bp[ee];
+    }
+    double l[MU];
+    int id[MU];
+#pragma unroll
+    for (int u = 0; u < MU; u++) {
+      const int ee = u * kWave + lane;
+      double sum = 0.0;
+#pragma unroll
+      for (int c = 0; c < MC; c++)
+        if (c < n_hc) sum += part[u][c];
+      for (int c = MC; c < n_hc; c++) sum += a.partials[((long)c * R + r) * E + min(ee, E - 1)];   // hidden > 4096
+      const bool ok = ee < E;
+      id[u] = ok ? ee : 0x7FFFFFFF;
+      l[u] = ok ? sum + (a.bias ? (double)bias[u] : 0.0) : -INFINITY;
+    }
+    // softmax normaliser
     double mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int ee = u * kWave + lane;
-      id[u] = ee < E ? ee : 0x7FFFFFFF;
-      l[u] = ee < E ? lgs[r * E + ee] : -INFINITY;
-      mx = fmax(mx, l[u]);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+    for (int u = 0; u < MU; u++) mx = fmax(mx, l[u]);
+    mx = wave_max(mx);
     double z = 0.0;
 #pragma unroll
-    for (int u = 0; u < 4; u++)
+    for (int u = 0; u < MU; u++)
       if (id[u] < E) z += exp(l[u] - mx);
-    z = wave_sum_d(z);
-    // sort the lane's 4 candidates (network of 5 compare-exchanges)
+    z = wave_sum(z);
+    // the lane's candidates sorted by the selection key (network of 5 compare-exchanges),
+    // so each round compares only the lanes' heads
     auto cx = [&](int i, int j) {
       if (better(l[j], id[j], l[i], id[i])) {
         const double tl = l[i]; l[i] = l[j]; l[j] = tl;
         const int ti = id[i]; id[i] = id[j]; id[j] = ti;
       }
     };
+    static_assert(MU == 4, "the sorting network orders four candidates");
     cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
-    int head = 0;
+    // K rounds: the best head wins, its lane pops it; lane j keeps the j-th winner
+    double my_w = 0.0;
+    int my_e = 0;
     for (int j = 0; j < K; j++) {
-      double bl = head < 4 ? l[0] : -INFINITY;
-      int be = head < 4 ? id[0] : 0x7FFFFFFF;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const double ol = __shfl_xor(bl, off);
-        const int oe = __shfl_xor(be, off);
-        if (better(ol, oe, bl, be)) { bl = ol; be = oe; }
-      }
-      if (head < 4 && id[0] == be) {   // the winner pops its head
+      double bl = l[0];
+      int be = id[0];
+      wave_argmax(bl, be);
+      if (id[0] == be) {
         l[0] = l[1]; l[1] = l[2]; l[2] = l[3]; l[3] = -INFINITY;
         id[0] = id[1]; id[1] = id[2]; id[2] = id[3]; id[3] = 0x7FFFFFFF;
-        head++;
       }
       if (lane == j) {
-        s_idx[r * K + j] = be;
-        s_w[r * K + j] = (float)(exp(bl - mx) / z);   // unnormalised copy, fixed below
-        lgs[r * E + be] = exp(bl - mx) / z;           // keep the double weight
+        my_e = be;
+        my_w = exp(bl - mx) / z;
       }
     }
-    // weights (renormalised over the row's k when asked), in selection order
+    // weights (divided by their sum over the row's k when asked), in selection order
+    if (a.renorm) my_w = my_w / wave_sum(lane < K ? my_w : 0.0);
     if (lane < K) {
-      const int be = s_idx[r * K + lane];
-      const double w = lgs[r * E + be];
-      double ssum = 0.0;
-      for (int j = 0; j < K; j++) ssum += lgs[r * E + s_idx[r * K + j]];
-      const double wf = a.renorm ? w / ssum : w;
-      a.topk_idx[r * K + lane] = be;
-      a.topk_w[r * K + lane] = (float)wf;
-      s_w[r * K + lane] = (float)wf;
+      a.topk_idx[r * K + lane] = my_e;
+      a.topk_w[r * K + lane] = (float)my_w;
+      s_wt[r][my_e] = (float)my_w;
+      atomicOr(&s_mask[my_e], 1u << r);
     }
   }
   __syncthreads();
 
-  // grouping: row mask per expert, then compaction in expert order (threads 0..255)
-  {
-    int tk[kMaxRows * 8];
+  // grouping: expert e = tid (waves 0..3); mask bit r = row r uses e
+  const int e = tid;
+  const uint32_t m = e < E ? s_mask[e] : 0u;
+  if (e <= E) a.row_mask[e] = (uint8_t)(e == E ? (1u << R) - 1u : m);
+  const bool used = m != 0u;
+  const int cnt = __builtin_popcount(m);
+  // positions within the wave: used experts below, entries of the experts below
+  const uint64_t bu = __ballot(used);
+  const int rank = lanes_below(bu);
+  int before = 0, wave_cnt = 0;   // cnt <= 8: four bit planes
 #pragma unroll
-    for (int t = 0; t < kMaxRows * 8; t += 4) {
-      const int4 v = *(const int4*)&s_idx[t];
-      tk[t] = v.x; tk[t + 1] = v.y; tk[t + 2] = v.z; tk[t + 3] = v.w;
-    }
-    for (int ee = tid; ee <= E; ee += kFinalThreads) {
-      uint32_t m = 0;
-      if (ee == E) {
-        m = (1u << R) - 1u;
-      } else {
-#pragma unroll
-        for (int t = 0; t < kMaxRows * 8; t++)
-          if (tk[t] == ee) m |= 1u << (t / K);
-      }
-      s_mask[ee] = m;
-      a.row_mask[ee] = (uint8_t)m;
-    }
+  for (int b = 0; b < 4; b++) {
+    const uint64_t plane = __ballot((cnt >> b) & 1);
+    before += lanes_below(plane) << b;
+    wave_cnt += __popcll(plane) << b;
   }
-  __syncthreads();
-
-  // exclusive scans of (used ? 1 : 0) and popcount over the routed experts (E <= 256:
-  // one expert per thread of waves 0..3)
-  const int ee = tid;
-  const uint32_t m = ee < E ? s_mask[ee] : 0u;
-  const int f = m != 0, c = __builtin_popcount(m);
-  int fi = f, ci = c;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int tf = __shfl_up(fi, off), tc = __shfl_up(ci, off);
-    if (lane >= off) { fi += tf; ci += tc; }
+  if (lane == 0 && wave < 4) {
+    s_tot[0][wave] = __popcll(bu);
+    s_tot[1][wave] = wave_cnt;
   }
-  if (lane == 63 && wave < 4) { s_wsum[0][wave] = fi; s_wsum[1][wave] = ci; }
   __syncthreads();
   if (wave >= 4) return;
   int pf = 0, pc = 0, tot_f = 0, tot_c = 0;
+#pragma unroll
   for (int w = 0; w < 4; w++) {
-    if (w < wave) { pf += s_wsum[0][w]; pc += s_wsum[1][w]; }
-    tot_f += s_wsum[0][w]; tot_c += s_wsum[1][w];
+    if (w < wave) { pf += s_tot[0][w]; pc += s_tot[1][w]; }
+    tot_f += s_tot[0][w];
+    tot_c += s_tot[1][w];
   }
-  if (f) {
-    const int pos = pf + fi - f, off = pc + ci - c;
-    a.active[pos] = ee;
+  if (used) {
+    const int pos = pf + rank, off = pc + before;
+    a.active[pos] = e;
     a.offsets[pos] = off;
-    // the expert's (row, weight) entries: top-k positions are row-major, so scanning
-    // them in order lists the rows ascending
-    int n = 0;
-#pragma unroll
-    for (int t = 0; t < kMaxRows * 8; t += 4) {
-      const int4 v = *(const int4*)&s_idx[t];
-      const int tv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int u = 0; u < 4; u++)
-        if (tv[u] == ee) {
-          a.entry_row[off + n] = (t + u) / K;
-          a.entry_w[off + n] = s_w[t + u];
-          n++;
-        }
+    // the expert's rows ascending, each with its weight
+    uint32_t mm = m;
+    for (int n = 0; mm; n++) {
+      const int r = __builtin_ctz(mm);
+      mm &= mm - 1u;
+      a.entry_row[off + n] = r;
+      a.entry_w[off + n] = s_wt[r][e];
     }
   }
   if (tid == 0) {
