@@ -46,7 +46,22 @@ def parse():
     p.add_argument("--windows", type=int, default=256, help="distinct activation windows")
     p.add_argument("--prof-steps", type=int, default=512, help="eager steps timed per kernel")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget (0: skip)")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="first copy this many MiB device to device three times (a dispatch of known "
+                        "bytes for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def calibration_copy(torch, mib):
+    """Three plain device-to-device copies of mib MiB (torch's copy kernel)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: 3 x {mib} MiB read + {mib} MiB written")
+    del src, dst
 
 
 def bpw(bits):
@@ -204,6 +219,8 @@ def main():
     import verify_window_expert_amd as sw
     sw.library()   # raises if the HIP library is not built
     DevLayer, to_dev_x = device_layer_types(torch, sw)
+    if args.calibrate_copy_mib > 0:
+        calibration_copy(torch, args.calibrate_copy_mib)
 
     if args.config == 3:
         return bench_stack(args, torch, synth, sw, DevLayer, to_dev_x)
