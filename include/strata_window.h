@@ -134,7 +134,8 @@ typedef struct {
  *   exact products; p = softmax over all experts; the top_k largest logits are selected.
  *   flags: 0 or STRATA_ROUTE_RENORM.
  * Errors: STRATA_EINVAL for a null or misaligned pointer, a bad dtype or flag, sizes
- * outside the limits, or a workspace smaller than strata_window_workspace(0, ...).
+ * outside the limits (hidden must be a multiple of 32), or a workspace smaller than
+ * strata_window_workspace(0, ...).
  */
 int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int hidden,
                         const float* gate_w, const float* logit_bias, int n_experts,

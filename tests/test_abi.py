@@ -82,7 +82,7 @@ def call_route(sw, rows=8, hidden=2048, E=128, k=8, flags=0, x=A, ws=A, ws_bytes
 @pytest.mark.parametrize("kw", [dict(rows=0), dict(rows=9), dict(k=0), dict(k=9), dict(E=4, k=8),
                                 dict(E=257), dict(flags=2), dict(x=0), dict(x=A + 8), dict(ws=0),
                                 dict(ws=A + 16), dict(ws_bytes=100), dict(dtype=2), dict(gate=0),
-                                dict(bias=A + 4), dict(hidden=0)])
+                                dict(bias=A + 4), dict(hidden=0), dict(hidden=2040)])
 def test_route_rejects(sw, kw):
     assert call_route(sw, **kw) == sw.STRATA_EINVAL
     assert sw.library().strata_window_last_error().decode() != ""

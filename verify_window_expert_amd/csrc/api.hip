@@ -160,6 +160,7 @@ int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int 
   int rc;
   if ((rc = check_common(x, x_dtype, rows, hidden, ws))) return rc;
   if ((rc = check_experts(n_experts, top_k))) return rc;
+  if (hidden % 32) return fail(STRATA_EINVAL, "hidden %d is not a multiple of 32", hidden);
   if (!gate_w || !aligned(gate_w, 16)) return fail(STRATA_EINVAL, "gate_w NULL or not 16-byte aligned");
   if (logit_bias && !aligned(logit_bias, 16)) return fail(STRATA_EINVAL, "logit_bias not 16-byte aligned");
   if (flags & ~STRATA_ROUTE_RENORM) return fail(STRATA_EINVAL, "unknown route flags 0x%x", flags);

@@ -22,80 +22,104 @@ constexpr int kMaxExpertsRoute = 256;     // the ABI's limit on experts
 
 template <bool F32IN>
 __global__ __launch_bounds__(256) void k_route_logits(RouteArgs a) {
-  __shared__ double xs[kMaxRows][kRouteChunk];
+  __shared__ __align__(16) double xs[kMaxRows][kRouteChunk];
 
-  const int H = a.hidden, E = a.n_experts, R = a.rows, K = a.top_k;
+  const int H = a.hidden, E = a.n_experts, R = a.rows;
   const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
   const int hc = blockIdx.x % n_hc, eg = blockIdx.x / n_hc;
   const int h0 = hc * kRouteChunk;
-  const int hn = min(kRouteChunk, H - h0);
+  const int hn = min(kRouteChunk, H - h0);   // a multiple of 32 (hidden % 32 == 0)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int e = eg * kRouteWaves + wave;
 
   // Every load below is unconditional with its index clamped into range, so a thread's
-  // loads issue back to back; values outside the range are masked afterwards.
-  // gate weights of this wave's expert: 8 loads in flight per lane
-  float gv[kRouteChunk / kWave];
-  const long erow = (long)min(e, E - 1) * H;
+  // loads issue back to back; values outside the range are zeroed afterwards.
+  // gate weights of this wave's expert: inputs 2*lane + 128u, 2*lane + 128u + 1
+  constexpr int NU = kRouteChunk / 128;
+  float2 gv[NU];
+  const float* grow = a.gate_w + (long)min(e, E - 1) * H + h0;
 #pragma unroll
-  for (int u = 0; u < kRouteChunk / kWave; u++) {
-    const int h = u * kWave + lane;
-    gv[u] = a.gate_w[erow + h0 + min(h, hn - 1)];
-  }
-  // the rows' inputs of this chunk as doubles (exact): thread handles inputs 2t, 2t+1 of
-  // every row
+  for (int u = 0; u < NU; u++) gv[u] = *(const float2*)(grow + min(128 * u + 2 * lane, hn - 2));
+  // the chunk of the window's rows, as doubles (exact): thread t converts row t / 32,
+  // inputs 16 (t % 32) .. +15; rows past R and inputs past hn become 0
   {
-    float xv[kMaxRows][2];
+    const int xr = tid >> 5, xc = 16 * (tid & 31);
+    const bool ok = xr < R && xc < hn;
+    const long base = (long)min(xr, R - 1) * H + h0 + min(xc, hn - 16);
+    float v[16];
+    if constexpr (F32IN) {
+      const u32x4* p = (const u32x4*)((const float*)a.x + base);
+      u32x4 w[4];
 #pragma unroll
-    for (int r = 0; r < kMaxRows; r++)
+      for (int i = 0; i < 4; i++) w[i] = p[i];
 #pragma unroll
-      for (int t = 0; t < 2; t++)
-        xv[r][t] = load_x<F32IN>(a.x, (long)min(r, R - 1) * H + h0 + min(2 * tid + t, hn - 1));
+      for (int i = 0; i < 16; i++) {
+        const uint32_t b = w[i >> 2][i & 3];
+        v[i] = __uint_as_float(b);
+      }
+    } else {
+      const u32x4* p = (const u32x4*)((const uint16_t*)a.x + base);
+      u32x4 w[2];
 #pragma unroll
-    for (int r = 0; r < kMaxRows; r++)
+      for (int i = 0; i < 2; i++) w[i] = p[i];
 #pragma unroll
-      for (int t = 0; t < 2; t++) xs[r][2 * tid + t] = (2 * tid + t < hn) ? (double)xv[r][t] : 0.0;
+      for (int i = 0; i < 16; i++) v[i] = bf16_to_f32((uint16_t)(w[i >> 3][(i >> 1) & 3] >> (16 * (i & 1))));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i += 2)
+      *(double2*)&xs[xr][xc + i] = double2{ok ? (double)v[i] : 0.0, ok ? (double)v[i + 1] : 0.0};
   }
 #pragma unroll
-  for (int u = 0; u < kRouteChunk / kWave; u++)
-    if (u * kWave + lane >= hn) gv[u] = 0.f;
+  for (int u = 0; u < NU; u++)
+    if (128 * u + 2 * lane >= hn) gv[u] = float2{0.f, 0.f};
   __syncthreads();
 
-  if (e < E) {
-    double acc[kMaxRows];
+  // all eight rows (rows past R read zeros), then eight independent wave sums
+  double acc[kMaxRows];
 #pragma unroll
-    for (int r = 0; r < kMaxRows; r++) acc[r] = 0.0;
+  for (int r = 0; r < kMaxRows; r++) acc[r] = 0.0;
 #pragma unroll
-    for (int u = 0; u < kRouteChunk / kWave; u++) {
-      const int h = u * kWave + lane;
-#pragma unroll
-      for (int r = 0; r < kMaxRows; r++)
-        if (r < R) acc[r] = fma((double)gv[u], xs[r][h], acc[r]);
-    }
+  for (int u = 0; u < NU; u++) {
+    const int h = 128 * u + 2 * lane;
 #pragma unroll
     for (int r = 0; r < kMaxRows; r++) {
-      if (r >= R) break;
-      const double s = wave_sum(acc[r]);
-      if (lane == 0) a.partials[((long)hc * R + r) * E + e] = s;
+      const double2 xv = *(const double2*)&xs[r][h];
+      acc[r] = fma((double)gv[u].x, xv.x, acc[r]);
+      acc[r] = fma((double)gv[u].y, xv.y, acc[r]);
     }
+  }
+  double sum[kMaxRows];
+#pragma unroll
+  for (int r = 0; r < kMaxRows; r++) sum[r] = wave_sum(acc[r]);
+  if (lane < kMaxRows && lane < R && e < E) {
+    double s = sum[0];
+#pragma unroll
+    for (int r = 1; r < kMaxRows; r++) s = lane == r ? sum[r] : s;
+    a.partials[((long)hc * R + lane) * E + e] = s;
   }
 }
 
-// Key order of the selection: larger logit first, then the lower expert index.
-__device__ __forceinline__ bool better(double l, int e, double lb, int eb) {
-  return l > lb || (l == lb && e < eb);
+// Selection key: larger logit first, then the lower expert index, as one unsigned 64-bit
+// integer. The double's bits map monotonically to an unsigned order (negative values
+// flipped whole, positive ones with the sign bit set); the low 8 bits then carry
+// 255 - expert. Two logits closer than 2^-44 of their magnitude (far below the ~1e-13
+// by which two summation orders of the same double sum differ) therefore order by
+// index; equal logits always do.
+__device__ __forceinline__ uint64_t select_key(double l, int e) {
+  uint64_t u = __builtin_bit_cast(uint64_t, l);
+  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return (u & ~0xFFull) | (uint64_t)(255 - e);
 }
+__device__ __forceinline__ int key_expert(uint64_t k) { return 255 - (int)(k & 0xFF); }
 
-// (logit, expert) of the wave's best candidate, in every lane.
-__device__ __forceinline__ void wave_argmax(double& l, int& e) {
-  Words<3> v{{(uint32_t)__builtin_bit_cast(uint64_t, l), (uint32_t)(__builtin_bit_cast(uint64_t, l) >> 32),
-              (uint32_t)e}};
-  v = wave_allreduce_words<3>(v, [](const Words<3>& p, const Words<3>& q) {
-    const double lp = double_of(Words<2>{{p.w[0], p.w[1]}}), lq = double_of(Words<2>{{q.w[0], q.w[1]}});
-    return better(lq, (int)q.w[2], lp, (int)p.w[2]) ? q : p;
+// The largest key of the wave, in every lane.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  const Words<2> w = wave_allreduce_words<2>(Words<2>{{(uint32_t)k, (uint32_t)(k >> 32)}},
+                                              [](const Words<2>& p, const Words<2>& q) {
+    const uint64_t a = (uint64_t)p.w[0] | ((uint64_t)p.w[1] << 32), b = (uint64_t)q.w[0] | ((uint64_t)q.w[1] << 32);
+    return a > b ? p : q;
   });
-  l = double_of(Words<2>{{v.w[0], v.w[1]}});
-  e = (int)v.w[2];
+  return (uint64_t)w.w[0] | ((uint64_t)w.w[1] << 32);
 }
 
 // popcount of the bits of m held by the lanes below this one
@@ -105,7 +129,7 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 constexpr int kFinalThreads = 512;   // one wave per window row
 
-// One workgroup: wave r adds row r's partials in chunk order, then softmax and top-k for
+// One workgroup: wave r adds row r's partials in chunk order, then top-k and softmax for
 // the row (every reduction inside the wave, without LDS); the row's selections go to LDS
 // as a row mask per expert and a weight per (row, expert); waves 0..3 then list the used
 // experts in ascending order with their rows (ballots give every position directly).
@@ -116,26 +140,28 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
   const int H = a.hidden, E = a.n_experts, R = a.rows, K = a.top_k;
   const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+
+  // logits of experts lane + 64u of row r = wave: every chunk's partial loaded at once
+  // (clamped, unconditional), added in chunk order below, then the bias
+  constexpr int MU = kMaxExpertsRoute / kWave, MC = 8;
+  const int r = min(wave, R - 1);
+  double part[MU][MC];
+  float bias[MU];
+  const float* bp = a.bias ? a.bias : a.gate_w;   // any readable array when unbiased
+#pragma unroll
+  for (int u = 0; u < MU; u++) {
+    const int ee = min(u * kWave + lane, E - 1);
+#pragma unroll
+    for (int c = 0; c < MC; c++) part[u][c] = a.partials[((long)min(c, n_hc - 1) * R + r) * E + ee];
+    bias[u] = bp[ee];
+  }
+  // (while those are in flight) clear the row masks
   for (int i = tid; i <= E; i += kFinalThreads) s_mask[i] = 0u;
   __syncthreads();
 
   if (wave < R) {
-    const int r = wave;
-    // logits of experts lane + 64u: every chunk's partial loaded at once (clamped,
-    // unconditional), added in chunk order, then the bias
-    constexpr int MU = kMaxExpertsRoute / kWave, MC = 8;
-    double part[MU][MC];
-    float bias[MU];
-    const float* bp = a.bias ? a.bias : a.gate_w;   // any readable array when unbiased
-#pragma unroll
-    for (int u = 0; u < MU; u++) {
-      const int ee = min(u * kWave + lane, E - 1);
-#pragma unroll
-      for (int c = 0; c < MC; c++) part[u][c] = a.partials[((long)min(c, n_hc - 1) * R + r) * E + ee];
-      bias[u] = bp[ee];
-    }
     double l[MU];
-    int id[MU];
+    uint64_t key[MU];
 #pragma unroll
     for (int u = 0; u < MU; u++) {
       const int ee = u * kWave + lane;
@@ -145,45 +171,47 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
         if (c < n_hc) sum += part[u][c];
       for (int c = MC; c < n_hc; c++) sum += a.partials[((long)c * R + r) * E + min(ee, E - 1)];   // hidden > 4096
       const bool ok = ee < E;
-      id[u] = ok ? ee : 0x7FFFFFFF;
       l[u] = ok ? sum + (a.bias ? (double)bias[u] : 0.0) : -INFINITY;
+      key[u] = ok ? select_key(l[u], ee) : 0ull;   // 0: below every real key
     }
-    // softmax normaliser
-    double mx = -INFINITY;
+    // the lane's keys sorted descending (network of 5 compare-exchanges), so each round
+    // compares only the lanes' heads
+    uint64_t hk[MU];
 #pragma unroll
-    for (int u = 0; u < MU; u++) mx = fmax(mx, l[u]);
-    mx = wave_max(mx);
-    double z = 0.0;
-#pragma unroll
-    for (int u = 0; u < MU; u++)
-      if (id[u] < E) z += exp(l[u] - mx);
-    z = wave_sum(z);
-    // the lane's candidates sorted by the selection key (network of 5 compare-exchanges),
-    // so each round compares only the lanes' heads
+    for (int u = 0; u < MU; u++) hk[u] = key[u];
     auto cx = [&](int i, int j) {
-      if (better(l[j], id[j], l[i], id[i])) {
-        const double tl = l[i]; l[i] = l[j]; l[j] = tl;
-        const int ti = id[i]; id[i] = id[j]; id[j] = ti;
-      }
+      const uint64_t a0 = hk[i], a1 = hk[j];
+      hk[i] = a0 > a1 ? a0 : a1;
+      hk[j] = a0 > a1 ? a1 : a0;
     };
     static_assert(MU == 4, "the sorting network orders four candidates");
     cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
-    // K rounds: the best head wins, its lane pops it; lane j keeps the j-th winner
-    double my_w = 0.0;
-    int my_e = 0;
+    // K rounds: the best head wins and its lane pops it; lane j keeps the j-th winner
+    uint64_t my_key = 0;
     for (int j = 0; j < K; j++) {
-      double bl = l[0];
-      int be = id[0];
-      wave_argmax(bl, be);
-      if (id[0] == be) {
-        l[0] = l[1]; l[1] = l[2]; l[2] = l[3]; l[3] = -INFINITY;
-        id[0] = id[1]; id[1] = id[2]; id[2] = id[3]; id[3] = 0x7FFFFFFF;
-      }
-      if (lane == j) {
-        my_e = be;
-        my_w = exp(bl - mx) / z;
-      }
+      const uint64_t best = wave_max_key(hk[0]);
+      if (hk[0] == best) { hk[0] = hk[1]; hk[1] = hk[2]; hk[2] = hk[3]; hk[3] = 0; }
+      if (lane == j) my_key = best;
     }
+    // softmax, then the K weights in parallel (lane j: the j-th winner)
+    const int my_e = key_expert(my_key);
+    double lmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MU; u++) lmax = fmax(lmax, l[u]);
+    lmax = wave_max(lmax);
+    double z = 0.0;
+#pragma unroll
+    for (int u = 0; u < MU; u++)
+      if (u * kWave + lane < E) z += exp(l[u] - lmax);
+    z = wave_sum(z);
+    // the winner's logit: lane j reads it from the lane that holds expert my_e
+    double lw = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MU; u++) {
+      const double v = __shfl(l[u], my_e & 63);
+      if ((my_e >> 6) == u) lw = v;
+    }
+    double my_w = exp(lw - lmax) / z;
     // weights (divided by their sum over the row's k when asked), in selection order
     if (a.renorm) my_w = my_w / wave_sum(lane < K ? my_w : 0.0);
     if (lane < K) {
