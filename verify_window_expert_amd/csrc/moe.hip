@@ -494,13 +494,14 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
 }
 
 // --------------------------------------------------------------------------- down
-// Persistent, 8-wave workgroups; workgroup b serves expert slot b % n_active (the
+// Persistent, 16-wave workgroups (so that each (slot, output tile) item gets a wave of
+// its own at the usual shapes); workgroup b serves expert slot b % n_active (the
 // workgroups of a slot split its output tiles) and stages that expert's h once; each
 // wave streams whole 16-row output tiles through the ring. y[entry][row] is written for
 // each of the expert's rows; k_combine sums them. As in gate/up, h (from L2) is staged
 // in LDS before the weights are requested.
 
-constexpr int kDnWaves = 8, kDnThreads = 64 * kDnWaves;
+constexpr int kDnWaves = 16, kDnThreads = 64 * kDnWaves;
 constexpr int kDownRange = 64;   // rows per combine workgroup
 
 template <int BITS, int XG>
@@ -762,9 +763,9 @@ static int launch_down_k(const DownArgs& a, size_t lds, int max_slots, hipStream
 template <int BITS>
 static int launch_down_bits(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
   // h groups (8 floats) of up to 8 rows per thread, all loaded up front (8 * ffn / 8)
+  if (a.ffn <= 1 * kDnThreads) return launch_down_k<BITS, 1>(a, lds, max_slots, s, p);
   if (a.ffn <= 2 * kDnThreads) return launch_down_k<BITS, 2>(a, lds, max_slots, s, p);
   if (a.ffn <= 4 * kDnThreads) return launch_down_k<BITS, 4>(a, lds, max_slots, s, p);
-  if (a.ffn <= 8 * kDnThreads) return launch_down_k<BITS, 8>(a, lds, max_slots, s, p);
   return (int)hipErrorInvalidValue;
 }
 
