@@ -127,7 +127,9 @@ class Steps:
                         offsets=torch.empty(steps, pad(A + 1), dtype=i32, device=dev),
                         entry_row=torch.empty(steps, pad(ent), dtype=i32, device=dev),
                         entry_w=torch.empty(steps, pad(ent), dtype=f32, device=dev),
-                        row_mask=torch.empty(steps, pad(E + 1), dtype=torch.uint8, device=dev))
+                        row_mask=torch.empty(steps, pad(E + 1), dtype=torch.uint8, device=dev),
+                        entry_pos=torch.empty(steps, pad(ent), dtype=i32, device=dev),
+                        row_w=torch.empty(steps, pad(R * (k + 1)), dtype=f32, device=dev))
         self.routes = []
         for i in range(steps):
             ro = sw.RouteOut.__new__(sw.RouteOut)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define STRATA_WINDOW_ABI_VERSION 1
+#define STRATA_WINDOW_ABI_VERSION 2
 
 enum { STRATA_OK = 0, STRATA_EINVAL = -1, STRATA_EUNSUPPORTED = -2, STRATA_EHIP = -3 };
 enum { STRATA_F32 = 0, STRATA_BF16 = 1 };       /* activation dtypes                */
@@ -110,7 +110,11 @@ typedef struct {
  *   entry_row[R*k+R] int32  row of each entry, ascending within an expert
  *   entry_w  [R*k+R] float  routing weight of each entry (1 for the shared expert)
  *   row_mask [E+1] uint8  bit r set when row r uses that expert (entry E: all rows)
- * Entries past n_active / offsets[n_active] are left untouched.
+ *   entry_pos[R*k+R] int32  position of each entry in its row's list of experts in
+ *                         ascending id order (routed 0..k-1, the shared expert k)
+ *   row_w  [R*(k+1)] float  row r's weights in that order (row_w[r*(k+1)+k] = 1)
+ * Entries past n_active / offsets[n_active] are left untouched. (entry_pos and row_w
+ * let strata_window_moe sum each row's experts in the fixed order with no search.)
  */
 typedef struct {
   int32_t* topk_idx;
@@ -121,6 +125,8 @@ typedef struct {
   int32_t* entry_row;
   float*   entry_w;
   uint8_t* row_mask;
+  int32_t* entry_pos;
+  float*   row_w;
 } strata_route_out;
 
 /*

@@ -73,6 +73,24 @@ def assert_route_equal(gr, orc, cfg):
     # the GPU rounds each double-precision weight to float (tiny ones to 0 or subnormal)
     np.testing.assert_allclose(gr["topk_w"], orc["w"].astype(np.float32), rtol=1e-6, atol=1e-44)
     np.testing.assert_allclose(gr["entry_w"], g["entry_w"].astype(np.float32), rtol=1e-6, atol=1e-44)
+    # each row's list of experts in ascending id order (shared last): every entry's place
+    # in it, and the row's weights in that order, derived here from the oracle's top-k
+    idx, w = orc["idx"], orc["w"]
+    R, K = idx.shape
+    place, row_w = {}, np.zeros((R, K + 1))
+    for r in range(R):
+        for p, j in enumerate(np.argsort(idx[r], kind="stable")):
+            place[(r, int(idx[r][j]))] = p
+            row_w[r, p] = w[r, j]
+        row_w[r, K] = 1.0
+    E = cfg.experts
+    want_pos = []
+    for a, e in enumerate(g["active"]):
+        for n in range(g["offsets"][a], g["offsets"][a + 1]):
+            r = int(g["entry_row"][n])
+            want_pos.append(K if e == E else place[(r, int(e))])
+    assert np.array_equal(gr["entry_pos"], np.array(want_pos)), (gr["entry_pos"], want_pos)
+    np.testing.assert_allclose(gr["row_w"], row_w.astype(np.float32), rtol=1e-6, atol=1e-44)
 
 
 # The tolerance the layer's outputs are held to: per row, max |gpu - oracle| over

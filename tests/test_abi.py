@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(sw):
 
 
 def test_abi_version(sw):
-    assert sw.library().strata_window_abi_version() == 1
+    assert sw.library().strata_window_abi_version() == 2
 
 
 def test_workspace_sizes(sw):
@@ -63,7 +63,7 @@ A = 0x10000000
 
 
 def route_out(sw, bad=None, misalign=None):
-    vals = [A + 0x1000 * i for i in range(8)]
+    vals = [A + 0x1000 * i for i in range(len(sw.CRouteOut._fields_))]
     names = [f[0] for f in sw.CRouteOut._fields_]
     if bad:
         vals[names.index(bad)] = 0
@@ -88,7 +88,7 @@ def test_route_rejects(sw, kw):
     assert sw.library().strata_window_last_error().decode() != ""
 
 
-@pytest.mark.parametrize("field", ["topk_idx", "active", "row_mask"])
+@pytest.mark.parametrize("field", ["topk_idx", "active", "row_mask", "entry_pos", "row_w"])
 def test_route_rejects_bad_outputs(sw, field):
     assert call_route(sw, ro=route_out(sw, bad=field)) == sw.STRATA_EINVAL
     assert call_route(sw, ro=route_out(sw, misalign=field)) == sw.STRATA_EINVAL

@@ -34,7 +34,8 @@ class CQMat(ctypes.Structure):
 
 class CRouteOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("topk_idx", "topk_w", "n_active", "active", "offsets", "entry_row", "entry_w", "row_mask")]
+                ("topk_idx", "topk_w", "n_active", "active", "offsets", "entry_row", "entry_w", "row_mask",
+                 "entry_pos", "row_w")]
 
 
 _lib = None
@@ -150,10 +151,13 @@ class RouteOut:
         self.entry_row = torch.empty(ent, **i32)
         self.entry_w = torch.empty(ent, dtype=torch.float32, device=device)
         self.row_mask = torch.empty(n_experts + 1, dtype=torch.uint8, device=device)
+        self.entry_pos = torch.empty(ent, **i32)
+        self.row_w = torch.empty(rows * (top_k + 1), dtype=torch.float32, device=device)
 
     def c(self):
         return CRouteOut(*(t.data_ptr() for t in (self.topk_idx, self.topk_w, self.n_active, self.active,
-                                                   self.offsets, self.entry_row, self.entry_w, self.row_mask)))
+                                                   self.offsets, self.entry_row, self.entry_w, self.row_mask,
+                                                   self.entry_pos, self.row_w)))
 
     def host(self):
         """Copy to the host as NumPy arrays, cut to the active length."""
@@ -164,7 +168,8 @@ class RouteOut:
                     topk_w=self.topk_w.view(self.rows, self.top_k).cpu().numpy(),
                     n_active=n, active=self.active[:n].cpu().numpy(), offsets=off,
                     entry_row=self.entry_row[:e].cpu().numpy(), entry_w=self.entry_w[:e].cpu().numpy(),
-                    row_mask=self.row_mask.cpu().numpy())
+                    row_mask=self.row_mask.cpu().numpy(), entry_pos=self.entry_pos[:e].cpu().numpy(),
+                    row_w=self.row_w.view(self.rows, self.top_k + 1).cpu().numpy())
 
 
 def workspace_bytes(which, rows, hidden, ffn=0, n_experts=0, top_k=0, vocab=0):

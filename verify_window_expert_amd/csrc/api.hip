@@ -80,9 +80,11 @@ int check_experts(int n_experts, int top_k) {
 
 int check_route_out(const strata_route_out* o) {
   if (!o) return fail(STRATA_EINVAL, "route output descriptor is NULL");
-  const void* p[] = {o->topk_idx, o->topk_w, o->n_active, o->active, o->offsets, o->entry_row, o->entry_w, o->row_mask};
-  const char* nm[] = {"topk_idx", "topk_w", "n_active", "active", "offsets", "entry_row", "entry_w", "row_mask"};
-  for (int i = 0; i < 8; i++) {
+  const void* p[] = {o->topk_idx, o->topk_w, o->n_active, o->active, o->offsets,
+                     o->entry_row, o->entry_w, o->row_mask, o->entry_pos, o->row_w};
+  const char* nm[] = {"topk_idx", "topk_w", "n_active", "active", "offsets",
+                      "entry_row", "entry_w", "row_mask", "entry_pos", "row_w"};
+  for (int i = 0; i < 10; i++) {
     if (!p[i]) return fail(STRATA_EINVAL, "route output %s is NULL", nm[i]);
     if (!aligned(p[i], 16)) return fail(STRATA_EINVAL, "route output %s is not 16-byte aligned", nm[i]);
   }
@@ -175,6 +177,7 @@ int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int 
   a.partials = (double*)((char*)ws + w.partials);
   a.topk_idx = out->topk_idx; a.topk_w = out->topk_w; a.n_active = out->n_active; a.active = out->active;
   a.offsets = out->offsets; a.entry_row = out->entry_row; a.entry_w = out->entry_w; a.row_mask = out->row_mask;
+  a.entry_pos = out->entry_pos; a.row_w = out->row_w;
   const sw::Prof pr = prof(prof_events, 0);
   return launch_status(sw::launch_route(a, (hipStream_t)stream, prof_events ? &pr : nullptr), "route");
 }
@@ -231,6 +234,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   d.down = qdev(down, sh_down);
   d.n_active = route->n_active; d.active = route->active; d.offsets = route->offsets;
   d.entry_row = route->entry_row; d.entry_w = route->entry_w; d.row_mask = route->row_mask;
+  d.entry_pos = route->entry_pos; d.row_w = route->row_w;
   d.h = g.h; d.y = (float*)((char*)ws + w.y); d.out = out; d.x_next = x_next_bf16;
   d.n_ranges = n_ranges; d.max_slots = max_slots; d.top_k = top_k;
   return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");

@@ -12,6 +12,7 @@ struct RouteArgs {
   double* partials;         // [chunk][row][expert]
   int32_t* topk_idx; float* topk_w; int32_t* n_active; int32_t* active; int32_t* offsets;
   int32_t* entry_row; float* entry_w; uint8_t* row_mask;
+  int32_t* entry_pos; float* row_w;
 };
 
 // One quantized matrix family: routed experts (stacked) and the shared expert.
@@ -37,8 +38,9 @@ struct DownArgs {
   QDev down;
   const int32_t* n_active; const int32_t* active; const int32_t* offsets;
   const int32_t* entry_row; const float* entry_w; const uint8_t* row_mask;
+  const int32_t* entry_pos; const float* row_w;
   const float* h;           // [entries][ffn]
-  float* y;                 // [entries][hidden]
+  float* y;                 // [rows][top_k + 1][hidden]: row r's experts in ascending id order
   float* out; uint16_t* x_next;
   int n_ranges;             // 64-row output ranges
   int max_slots, top_k;     // capacity of the active / offsets arrays; routing top-k

@@ -36,7 +36,10 @@ constexpr int kMaxSlots = kMaxRows * kMaxTopk + 1;   // routed experts a window 
 #define SW_GU_DEPTH 4
 #endif
 constexpr int kGuDepth = SW_GU_DEPTH;                // gate/up: units in flight per wave (ring slots)
-constexpr int kDnDepth = 8;                          // down: units in flight per wave
+#ifndef SW_DN_DEPTH
+#define SW_DN_DEPTH 4
+#endif
+constexpr int kDnDepth = SW_DN_DEPTH;                // down: units in flight per wave
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), unrolled: ring
 // slots are then compile-time register arrays.
@@ -497,8 +500,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
 // Persistent, 16-wave workgroups (so that each (slot, output tile) item gets a wave of
 // its own at the usual shapes); workgroup b serves expert slot b % n_active (the
 // workgroups of a slot split its output tiles) and stages that expert's h once; each
-// wave streams whole 16-row output tiles through the ring. y[entry][row] is written for
-// each of the expert's rows; k_combine sums them. As in gate/up, h (from L2) is staged
+// wave streams whole 16-row output tiles through the ring. y is written for each of the
+// expert's rows at that row's place in its ascending list of experts; k_combine sums
+// each row's list in order. As in gate/up, h (from L2) is staged
 // in LDS before the weights are requested.
 
 constexpr int kDnWaves = 16, kDnThreads = 64 * kDnWaves;
@@ -508,6 +512,7 @@ template <int BITS, int XG>
 __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   constexpr int DEPTH = kDnDepth;
   extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_ydst[kMaxRows];
   const int H = a.hidden, F = a.ffn, E = a.n_experts;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   constexpr int G = 512 / BITS;
@@ -533,12 +538,16 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   const int my_tiles = t0 < tiles_h ? (tiles_h - t0 + stride - 1) / stride : 0;
   const int units = my_tiles * NG;
 
-  // the expert's h (XG groups of 8 per thread)
+  // the expert's h (XG groups of 8 per thread), and where each of its entries' y goes:
+  // row r's list of experts in ascending id order, position entry_pos
   const ActLds l = act_lds(smem, F, 16);
   const float* hsrc = a.h + (long)e0 * F;
   u32x4 hr[XG][2];
   load_groups<kDnThreads, XG, true>(hr, hsrc, max(ne, 1), F);
+  const int ej = e0 + min(lane, max(ne, 1) - 1);
+  const int dst_row = a.entry_row[ej], dst_pos = a.entry_pos[ej];
   __builtin_amdgcn_sched_barrier(0);
+  if (tid < kMaxRows) s_ydst[tid] = dst_row * (a.top_k + 1) + dst_pos;
 
   // h into LDS before any weight is requested (as in gate/up)
   zero_absent<kDnThreads>(l, F, ne, true);
@@ -579,7 +588,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int j = 4 * q + i;
-          if (j < ne) a.y[(long)(e0 + j) * H + tile * 16 + c] = acc[i];
+          if (j < ne) a.y[(long)s_ydst[j] * H + tile * 16 + c] = acc[i];
         }
       }
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -590,78 +599,56 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
 }
 
 // ------------------------------------------------------------------------ combine
-// Workgroup = 64 output rows of every window row: row r's entries in ascending expert
-// order (the shared expert last), weighted, then the residual.
+// Thread = 4 consecutive outputs of one row: the row's k + 1 expert outputs are already
+// in its list order (routed experts ascending, the shared expert last) in y, and its
+// weights in the same order in row_w, so every load is issued at once (clamped; slots
+// past k + 1 are not summed), then the fixed-order sum and the residual.
+
+constexpr int kCombineThreads = 256;
 
 template <bool F32IN>
-__global__ __launch_bounds__(kThreads) void k_combine(DownArgs a) {
-  __shared__ int s_active[kMaxSlots], s_off[kMaxSlots + 1];
-  __shared__ uint8_t s_mask[kMaxExperts + 4];
-  __shared__ float s_ew[kMaxRows * kMaxTopk + kMaxRows];
-  __shared__ int s_list[kMaxRows][kMaxTopk + 2];
-  __shared__ float s_w[kMaxRows][kMaxTopk + 2];
-  __shared__ int s_cnt[kMaxRows];
-  const int H = a.hidden, R = a.rows, E = a.n_experts;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n_active = *a.n_active;
-  // every slot's metadata in one round (clamped loads; the arrays hold max_slots,
-  // max_slots + 1, E + 1 and R*k + R entries)
-  {
-    const int sa = a.active[min(tid, a.max_slots - 1)];
-    const int so = a.offsets[min(tid, a.max_slots)];
-    const uint8_t sm = a.row_mask[min(tid, E)], sm2 = a.row_mask[min(tid + kThreads, E)];
-    const int ne = R * a.top_k + R;
-    const float ew = a.entry_w[min(tid, ne - 1)];
-    if (tid < a.max_slots) s_active[tid] = sa;
-    if (tid <= a.max_slots) s_off[tid] = so;
-    if (tid <= E) s_mask[tid] = sm;
-    if (tid + kThreads <= E) s_mask[tid + kThreads] = sm2;
-    if (tid < ne) s_ew[tid] = ew;
-    if (tid < kMaxRows * (kMaxTopk + 2)) { (&s_list[0][0])[tid] = 0; (&s_w[0][0])[tid] = 0.f; }
-  }
-  __syncthreads();
-  // row r's entries in ascending expert order: one ballot per row over the slots
-  if (wave == 0) {
-    int base[kMaxRows] = {0};
-    for (int s0 = 0; s0 < n_active; s0 += 64) {
-      const int s = s0 + lane;
-      const bool ok = s < n_active;
-      const uint32_t m = ok ? s_mask[s_active[s]] : 0u;
+__global__ __launch_bounds__(kCombineThreads) void k_combine(DownArgs a) {
+  const int H = a.hidden, R = a.rows, K1 = a.top_k + 1;
+  const int H4 = H / 4;
+  const int t = blockIdx.x * kCombineThreads + threadIdx.x;
+  if (t >= R * H4) return;
+  const int r = t / H4, n = 4 * (t % H4);
+  float w[kMaxTopk + 1];
+  f32x4 yv[kMaxTopk + 1];
 #pragma unroll
-      for (int r = 0; r < kMaxRows; r++) {
-        if (r >= R) break;
-        const bool has = (m >> r) & 1u;
-        const uint64_t bal = __ballot(has);
-        if (has) {
-          const int pos = base[r] + __popcll(bal & ((1ull << lane) - 1ull));
-          const int ent = s_off[s] + __builtin_popcount(m & ((1u << r) - 1u));
-          s_list[r][pos] = ent;
-          s_w[r][pos] = s_ew[ent];
-        }
-        base[r] += __popcll(bal);
-      }
+  for (int j = 0; j <= kMaxTopk; j++) {
+    const int jj = min(j, K1 - 1);
+    w[j] = a.row_w[r * K1 + jj];
+    yv[j] = *(const f32x4*)(a.y + (long)(r * K1 + jj) * H + n);
+  }
+  float res[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.x_res) {
+    if constexpr (F32IN) {
+      const f32x4 v = *(const f32x4*)((const float*)a.x_res + (long)r * H + n);
+#pragma unroll
+      for (int i = 0; i < 4; i++) res[i] = v[i];
+    } else {
+      const uint2 v = *(const uint2*)((const uint16_t*)a.x_res + (long)r * H + n);
+      res[0] = bf16_to_f32((uint16_t)v.x); res[1] = bf16_to_f32((uint16_t)(v.x >> 16));
+      res[2] = bf16_to_f32((uint16_t)v.y); res[3] = bf16_to_f32((uint16_t)(v.y >> 16));
     }
-#pragma unroll
-    for (int r = 0; r < kMaxRows; r++)
-      if (r < R && lane == r) s_cnt[r] = base[r];
   }
-  __syncthreads();
-  const int n0 = blockIdx.x * kDownRange;
-  for (int idx = tid; idx < R * kDownRange; idx += kThreads) {
-    const int r = idx / kDownRange, n = n0 + idx % kDownRange;
-    if (n >= H) continue;
-    const int cnt = s_cnt[r];
-    float yv[kMaxTopk + 2];   // unused slots read entry 0 and are not summed
+  f32x4 o;
 #pragma unroll
-    for (int t = 0; t < kMaxTopk + 2; t++) yv[t] = a.y[(long)s_list[r][t] * H + n];
-    const float res = a.x_res ? load_x<F32IN>(a.x_res, (long)r * H + n) : 0.f;
+  for (int i = 0; i < 4; i++) {
     float s = 0.f;
 #pragma unroll
-    for (int t = 0; t < kMaxTopk + 2; t++)
-      if (t < cnt) s = fmaf(s_w[r][t], yv[t], s);
-    if (a.x_res) s += res;
-    a.out[(long)r * H + n] = s;
-    if (a.x_next) a.x_next[(long)r * H + n] = f32_to_bf16(s);
+    for (int j = 0; j <= kMaxTopk; j++)
+      if (j < K1) s = fmaf(w[j], yv[j][i], s);
+    if (a.x_res) s += res[i];
+    o[i] = s;
+  }
+  *(f32x4*)(a.out + (long)r * H + n) = o;
+  if (a.x_next) {
+    uint2 b;
+    b.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    b.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    *(uint2*)(a.x_next + (long)r * H + n) = b;
   }
 }
 
@@ -776,10 +763,11 @@ int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p) 
   const int e = a.bits == 4 ? launch_down_bits<4>(a, lds, max_slots, s, p ? &p0 : nullptr)
                             : launch_down_bits<2>(a, lds, max_slots, s, p ? &p0 : nullptr);
   if (e) return e;
+  const int cg = (a.rows * (a.hidden / 4) + kCombineThreads - 1) / kCombineThreads;
   if (a.x_dtype == 0)
-    launch(k_combine<true>, dim3(a.n_ranges), dim3(kThreads), 0, s, p ? &p1 : nullptr, a);
+    launch(k_combine<true>, dim3(cg), dim3(kCombineThreads), 0, s, p ? &p1 : nullptr, a);
   else
-    launch(k_combine<false>, dim3(a.n_ranges), dim3(kThreads), 0, s, p ? &p1 : nullptr, a);
+    launch(k_combine<false>, dim3(cg), dim3(kCombineThreads), 0, s, p ? &p1 : nullptr, a);
   return (int)hipGetLastError();
 }
 

@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
   __shared__ uint32_t s_mask[kMaxExpertsRoute + 1];
   __shared__ float s_wt[kMaxRows][kMaxExpertsRoute];
   __shared__ int s_tot[2][4];
+  __shared__ int s_rowcnt[4][kMaxRows];
   const int H = a.hidden, E = a.n_experts, R = a.rows, K = a.top_k;
   const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -239,9 +240,15 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
     before += lanes_below(plane) << b;
     wave_cnt += __popcll(plane) << b;
   }
+  // per row r: the experts of row r below this one (its position in the row's list)
+  uint64_t brow[kMaxRows];
+#pragma unroll
+  for (int rr = 0; rr < kMaxRows; rr++) brow[rr] = __ballot((m >> rr) & 1u);
   if (lane == 0 && wave < 4) {
     s_tot[0][wave] = __popcll(bu);
     s_tot[1][wave] = wave_cnt;
+#pragma unroll
+    for (int rr = 0; rr < kMaxRows; rr++) s_rowcnt[wave][rr] = __popcll(brow[rr]);
   }
   __syncthreads();
   if (wave >= 4) return;
@@ -252,17 +259,34 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
     tot_f += s_tot[0][w];
     tot_c += s_tot[1][w];
   }
+  const int K1 = K + 1;
+  // this expert's place in each row's list: experts of that row in lower waves + below
+  // this lane in its wave
+  int place[kMaxRows];
+#pragma unroll
+  for (int rr = 0; rr < kMaxRows; rr++) {
+    int p = lanes_below(brow[rr]);
+#pragma unroll
+    for (int w = 0; w < 3; w++)
+      if (w < wave) p += s_rowcnt[w][rr];
+    place[rr] = p;
+  }
   if (used) {
     const int pos = pf + rank, off = pc + before;
     a.active[pos] = e;
     a.offsets[pos] = off;
-    // the expert's rows ascending, each with its weight
-    uint32_t mm = m;
-    for (int n = 0; mm; n++) {
-      const int r = __builtin_ctz(mm);
-      mm &= mm - 1u;
-      a.entry_row[off + n] = r;
-      a.entry_w[off + n] = s_wt[r][e];
+    // the expert's rows ascending, each with its weight and its place in the row's list
+    int n = 0;
+#pragma unroll
+    for (int rr = 0; rr < kMaxRows; rr++) {
+      if ((m >> rr) & 1u) {
+        const float wt = s_wt[rr][e];
+        a.entry_row[off + n] = rr;
+        a.entry_w[off + n] = wt;
+        a.entry_pos[off + n] = place[rr];
+        a.row_w[rr * K1 + place[rr]] = wt;
+        n++;
+      }
     }
   }
   if (tid == 0) {
@@ -274,6 +298,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
   if (tid < R) {
     a.entry_row[tot_c + tid] = tid;
     a.entry_w[tot_c + tid] = 1.0f;
+    a.entry_pos[tot_c + tid] = K;
+    a.row_w[tid * K1 + K] = 1.0f;
   }
 }
 
