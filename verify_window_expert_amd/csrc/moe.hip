@@ -319,9 +319,9 @@ __device__ __forceinline__ void run_ring(int units, Step&& step) {
 // (so the result does not depend on which arrives first) and writes h. Items go to
 // groups wave-major (item i: workgroup i % grid) so every compute unit gets a share.
 //
-// Start-up: the activations, the routing tables and (by wave-uniform scalar loads) the
-// experts of each wave's first items are loaded in one round and staged in LDS before
-// the first ring of weight units is requested.
+// Start-up: the activations, the routing tables and the active count are loaded in one
+// round; each wave then requests its first ring of weights and only then stages the
+// activation image in LDS, so the staging overlaps the weights' flight.
 
 constexpr int kGuWaves = 8, kGuThreads = 64 * kGuWaves;
 constexpr size_t kPartBytes = (size_t)kGuWaves * 2 * 32 * 8 * 4;   // [wave][parity][lane < 32][8]
@@ -356,6 +356,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   const int sa = a.active[min(tid, a.max_slots - 1)];
   const int so = a.offsets[min(tid, a.max_slots)];
   const uint8_t sm = a.row_mask[min(tid, E)];
+  // every wave's own copy of the active list (lane i: slots i and 64 + i), for the
+  // experts of its first units before the LDS tables exist
+  const int act0 = a.active[min(lane, a.max_slots - 1)], act1 = a.active[min(64 + lane, a.max_slots - 1)];
   __builtin_amdgcn_sched_barrier(0);
 
   // the active count: a wave-uniform scalar load in the same round
@@ -393,24 +396,37 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
       }
     }
   };
-  // The activation image, the tables and the split counters go into LDS before any
-  // weight is requested: the prologue's loads then meet an idle memory system (behind
-  // other waves' weight streams they would take several times as long, and the
-  // barrier waits for the slowest wave of the workgroup).
-  if (tid < a.max_slots) s_active[tid] = sa;
-  if (tid <= a.max_slots) s_off[tid] = so;
-  if (tid <= E) s_mask[tid] = sm;
-  if (tid < kGuWaves * 2) { (&s_cnt[0][0])[tid] = 0; (&s_done[0][0])[tid] = 0; }
-  zero_absent<kGuThreads>(l, H, R, F32IN);
-  stage_groups<kGuThreads, XG, F32IN>(l, xr, R, H);   // the launcher picks XG to cover all groups
+  // The first ring of weights is requested as soon as this round's loads are back (the
+  // experts come from the wave's copy of the active list); the activation image, the
+  // tables and the split counters go into LDS while those weights are in flight. A wave
+  // without items takes a path of its own, so that in the working one the compiler sees
+  // exactly the weight loads issued after the round and waits for the round only.
+  auto stage = [&]() __attribute__((always_inline)) {
+    if (tid < a.max_slots) s_active[tid] = sa;
+    if (tid <= a.max_slots) s_off[tid] = so;
+    if (tid <= E) s_mask[tid] = sm;
+    if (tid < kGuWaves * 2) { (&s_cnt[0][0])[tid] = 0; (&s_done[0][0])[tid] = 0; }
+    zero_absent<kGuThreads>(l, H, R, F32IN);
+    stage_groups<kGuThreads, XG, F32IN>(l, xr, R, H);   // the launcher picks XG to cover all groups
+  };
+  if (units == 0) {
+    stage();
+    __syncthreads();
+    return;
+  }
+  auto reg_of = [&](int j) __attribute__((always_inline)) {
+    const int slot = min((me + j * Wg) / tiles, a.max_slots - 1);
+    return slot < 64 ? __builtin_amdgcn_readlane(act0, slot) : __builtin_amdgcn_readlane(act1, slot - 64);
+  };
+  set_item(reg_of(0), 0);
+  static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { issue_next(d, reg_of); });
+  __builtin_amdgcn_sched_barrier(0);
+  stage();
   __syncthreads();
-  if (units == 0) return;
-  // the expert of item ordinal j (the table in LDS)
+  // from here on, the expert of item ordinal j comes from the LDS table
   auto lds_of = [&](int j) __attribute__((always_inline)) {
     return __builtin_amdgcn_readfirstlane(s_active[min((me + j * Wg) / tiles, kMaxSlots - 1)]);
   };
-  set_item(lds_of(0), 0);
-  static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { issue_next(d, lds_of); });
 
   const int c = lane & 15, q = lane >> 4;
   const ActLane al = act_lane(l, (c & 7) < R && (c < 8 || F32IN));
@@ -547,14 +563,20 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   const int ej = e0 + min(lane, max(ne, 1) - 1);
   const int dst_row = a.entry_row[ej], dst_pos = a.entry_pos[ej];
   __builtin_amdgcn_sched_barrier(0);
-  if (tid < kMaxRows) s_ydst[tid] = dst_row * (a.top_k + 1) + dst_pos;
 
-  // h into LDS before any weight is requested (as in gate/up)
-  zero_absent<kDnThreads>(l, F, ne, true);
-  stage_groups<kDnThreads, XG, true>(l, hr, ne, F);   // the launcher picks XG to cover all groups
-  __syncthreads();
-  if (units == 0) return;
-
+  // then the first ring of weights (h and the entry table, requested first, come back
+  // first), and h goes into LDS while the weights are in flight; a wave without tiles
+  // takes a path of its own (as in gate/up)
+  auto stage = [&]() __attribute__((always_inline)) {
+    if (tid < kMaxRows) s_ydst[tid] = dst_row * (a.top_k + 1) + dst_pos;
+    zero_absent<kDnThreads>(l, F, ne, true);
+    stage_groups<kDnThreads, XG, true>(l, hr, ne, F);   // the launcher picks XG to cover all groups
+  };
+  if (units == 0) {
+    stage();
+    __syncthreads();
+    return;
+  }
   KGroup<BITS> kg[DEPTH];
   int is_j = 0, is_g = 0;
   TileRsrc pd = tile_rsrc<BITS>(a.down, e, E, t0, NG);
@@ -570,6 +592,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
     }
   };
   static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { issue_next(d); });
+  __builtin_amdgcn_sched_barrier(0);
+  stage();
+  __syncthreads();
 
   const int c = lane & 15, q = lane >> 4;
   const ActLane al = act_lane(l, (c & 7) < ne);
@@ -599,43 +624,42 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
 }
 
 // ------------------------------------------------------------------------ combine
-// Thread = 4 consecutive outputs of one row: the row's k + 1 expert outputs are already
+// Thread = 2 consecutive outputs of one row: the row's k + 1 expert outputs are already
 // in its list order (routed experts ascending, the shared expert last) in y, and its
 // weights in the same order in row_w, so every load is issued at once (clamped; slots
 // past k + 1 are not summed), then the fixed-order sum and the residual.
 
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 256, kCombineVec = 2;
 
 template <bool F32IN>
 __global__ __launch_bounds__(kCombineThreads) void k_combine(DownArgs a) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int H = a.hidden, R = a.rows, K1 = a.top_k + 1;
-  const int H4 = H / 4;
+  const int HV = H / kCombineVec;
   const int t = blockIdx.x * kCombineThreads + threadIdx.x;
-  if (t >= R * H4) return;
-  const int r = t / H4, n = 4 * (t % H4);
+  if (t >= R * HV) return;
+  const int r = t / HV, n = kCombineVec * (t % HV);
   float w[kMaxTopk + 1];
-  f32x4 yv[kMaxTopk + 1];
+  f32x2 yv[kMaxTopk + 1];
 #pragma unroll
   for (int j = 0; j <= kMaxTopk; j++) {
     const int jj = min(j, K1 - 1);
     w[j] = a.row_w[r * K1 + jj];
-    yv[j] = *(const f32x4*)(a.y + (long)(r * K1 + jj) * H + n);
+    yv[j] = *(const f32x2*)(a.y + (long)(r * K1 + jj) * H + n);
   }
-  float res[4] = {0.f, 0.f, 0.f, 0.f};
+  float res[2] = {0.f, 0.f};
   if (a.x_res) {
     if constexpr (F32IN) {
-      const f32x4 v = *(const f32x4*)((const float*)a.x_res + (long)r * H + n);
-#pragma unroll
-      for (int i = 0; i < 4; i++) res[i] = v[i];
+      const f32x2 v = *(const f32x2*)((const float*)a.x_res + (long)r * H + n);
+      res[0] = v[0]; res[1] = v[1];
     } else {
-      const uint2 v = *(const uint2*)((const uint16_t*)a.x_res + (long)r * H + n);
-      res[0] = bf16_to_f32((uint16_t)v.x); res[1] = bf16_to_f32((uint16_t)(v.x >> 16));
-      res[2] = bf16_to_f32((uint16_t)v.y); res[3] = bf16_to_f32((uint16_t)(v.y >> 16));
+      const uint32_t v = *(const uint32_t*)((const uint16_t*)a.x_res + (long)r * H + n);
+      res[0] = bf16_to_f32((uint16_t)v); res[1] = bf16_to_f32((uint16_t)(v >> 16));
     }
   }
-  f32x4 o;
+  f32x2 o;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < 2; i++) {
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j <= kMaxTopk; j++)
@@ -643,13 +667,9 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DownArgs a) {
     if (a.x_res) s += res[i];
     o[i] = s;
   }
-  *(f32x4*)(a.out + (long)r * H + n) = o;
-  if (a.x_next) {
-    uint2 b;
-    b.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-    b.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    *(uint2*)(a.x_next + (long)r * H + n) = b;
-  }
+  *(f32x2*)(a.out + (long)r * H + n) = o;
+  if (a.x_next)
+    *(uint32_t*)(a.x_next + (long)r * H + n) = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
 }
 
 // ------------------------------------------------------------------------ launchers
@@ -763,7 +783,7 @@ int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p) 
   const int e = a.bits == 4 ? launch_down_bits<4>(a, lds, max_slots, s, p ? &p0 : nullptr)
                             : launch_down_bits<2>(a, lds, max_slots, s, p ? &p0 : nullptr);
   if (e) return e;
-  const int cg = (a.rows * (a.hidden / 4) + kCombineThreads - 1) / kCombineThreads;
+  const int cg = (a.rows * (a.hidden / kCombineVec) + kCombineThreads - 1) / kCombineThreads;
   if (a.x_dtype == 0)
     launch(k_combine<true>, dim3(cg), dim3(kCombineThreads), 0, s, p ? &p1 : nullptr, a);
   else
