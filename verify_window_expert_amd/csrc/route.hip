@@ -142,19 +142,25 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
   const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
-  // logits of experts lane + 64u of row r = wave: every chunk's partial loaded at once
-  // (clamped, unconditional), added in chunk order below, then the bias
+  // logits of experts lane + 64u of row r = wave: every chunk's partial loaded at once,
+  // added in chunk order below, then the bias. Only the rows, chunks and expert quarters
+  // that exist are loaded (wave-uniform branches): one workgroup issues every load, so
+  // clamped duplicates would cost issue slots on its compute unit.
   constexpr int MU = kMaxExpertsRoute / kWave, MC = 8;
   const int r = min(wave, R - 1);
-  double part[MU][MC];
-  float bias[MU];
+  double part[MU][MC] = {};
+  float bias[MU] = {};
   const float* bp = a.bias ? a.bias : a.gate_w;   // any readable array when unbiased
+  if (wave < R) {
 #pragma unroll
-  for (int u = 0; u < MU; u++) {
-    const int ee = min(u * kWave + lane, E - 1);
+    for (int u = 0; u < MU; u++) {
+      if (u * kWave >= E) break;
+      const int ee = min(u * kWave + lane, E - 1);
 #pragma unroll
-    for (int c = 0; c < MC; c++) part[u][c] = a.partials[((long)min(c, n_hc - 1) * R + r) * E + ee];
-    bias[u] = bp[ee];
+      for (int c = 0; c < MC; c++)
+        if (c < n_hc) part[u][c] = a.partials[((long)c * R + r) * E + ee];
+      if (a.bias) bias[u] = bp[ee];
+    }
   }
   // (while those are in flight) clear the row masks
   for (int i = tid; i <= E; i += kFinalThreads) s_mask[i] = 0u;
