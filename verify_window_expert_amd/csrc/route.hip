@@ -129,10 +129,33 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 constexpr int kFinalThreads = 512;   // one wave per window row
 
+// The largest 32-bit value of the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_allreduce_words<1>(Words<1>{{v}}, [](const Words<1>& p, const Words<1>& q) {
+    return Words<1>{{p.w[0] > q.w[0] ? p.w[0] : q.w[0]}};
+  }).w[0];
+}
+
+// exp(d) for d <= 0 as a float: 2^t with t = d log2(e) split in double into an integer n
+// and a fraction f in [-1/2, 1/2]; 2^f by the hardware's exp2 (f rounded to float moves
+// it by at most 2^-25, i.e. 2e-8 relative), then scaled by 2^n.
+__device__ __forceinline__ float exp_nonpos(double d) {
+  const double t = fmax(d * 1.4426950408889634, -1000.0);
+  const double n = rint(t);
+  return ldexpf(__builtin_amdgcn_exp2f((float)(t - n)), (int)n);
+}
+
 // One workgroup: wave r adds row r's partials in chunk order, then top-k and softmax for
 // the row (every reduction inside the wave, without LDS); the row's selections go to LDS
 // as a row mask per expert and a weight per (row, expert); waves 0..3 then list the used
 // experts in ascending order with their rows (ballots give every position directly).
+//
+// Lane l holds experts MU*l .. MU*l + MU - 1. Top-k takes K rounds; in each, the lanes'
+// best remaining keys are compared on their upper 32 bits (one DPP max), and only when
+// several lanes share the largest upper half are those lanes' whole keys compared. The
+// winner's lane pops it. The softmax shift is the first winner's logit; the denominator
+// (double sum of float exponentials) does not depend on the later rounds.
+template <int MU>
 __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
   __shared__ uint32_t s_mask[kMaxExpertsRoute + 1];
   __shared__ float s_wt[kMaxRows][kMaxExpertsRoute];
@@ -142,24 +165,20 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
   const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
-  // logits of experts lane + 64u of row r = wave: every chunk's partial loaded at once,
-  // added in chunk order below, then the bias. Only the rows, chunks and expert quarters
-  // that exist are loaded (wave-uniform branches): one workgroup issues every load, so
-  // clamped duplicates would cost issue slots on its compute unit.
-  constexpr int MU = kMaxExpertsRoute / kWave, MC = 8;
+  // every chunk's partial loaded at once (only the rows and chunks that exist: one
+  // workgroup issues every load), added in chunk order below, then the bias
+  constexpr int MC = 8;
   const int r = min(wave, R - 1);
   double part[MU][MC] = {};
   float bias[MU] = {};
-  const float* bp = a.bias ? a.bias : a.gate_w;   // any readable array when unbiased
   if (wave < R) {
 #pragma unroll
     for (int u = 0; u < MU; u++) {
-      if (u * kWave >= E) break;
-      const int ee = min(u * kWave + lane, E - 1);
+      const int ee = min(MU * lane + u, E - 1);
 #pragma unroll
       for (int c = 0; c < MC; c++)
         if (c < n_hc) part[u][c] = a.partials[((long)c * R + r) * E + ee];
-      if (a.bias) bias[u] = bp[ee];
+      if (a.bias) bias[u] = a.bias[ee];
     }
   }
   // (while those are in flight) clear the row masks
@@ -168,10 +187,10 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
 
   if (wave < R) {
     double l[MU];
-    uint64_t key[MU];
+    uint64_t hk[MU];
 #pragma unroll
     for (int u = 0; u < MU; u++) {
-      const int ee = u * kWave + lane;
+      const int ee = MU * lane + u;
       double sum = 0.0;
 #pragma unroll
       for (int c = 0; c < MC; c++)
@@ -179,46 +198,67 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
       for (int c = MC; c < n_hc; c++) sum += a.partials[((long)c * R + r) * E + min(ee, E - 1)];   // hidden > 4096
       const bool ok = ee < E;
       l[u] = ok ? sum + (a.bias ? (double)bias[u] : 0.0) : -INFINITY;
-      key[u] = ok ? select_key(l[u], ee) : 0ull;   // 0: below every real key
+      hk[u] = ok ? select_key(l[u], ee) : 0ull;   // 0: below every real key
     }
-    // the lane's keys sorted descending (network of 5 compare-exchanges), so each round
-    // compares only the lanes' heads
-    uint64_t hk[MU];
-#pragma unroll
-    for (int u = 0; u < MU; u++) hk[u] = key[u];
+    // the lane's keys sorted descending
     auto cx = [&](int i, int j) {
       const uint64_t a0 = hk[i], a1 = hk[j];
       hk[i] = a0 > a1 ? a0 : a1;
       hk[j] = a0 > a1 ? a1 : a0;
     };
-    static_assert(MU == 4, "the sorting network orders four candidates");
-    cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
-    // K rounds: the best head wins and its lane pops it; lane j keeps the j-th winner
-    uint64_t my_key = 0;
-    for (int j = 0; j < K; j++) {
-      const uint64_t best = wave_max_key(hk[0]);
-      if (hk[0] == best) { hk[0] = hk[1]; hk[1] = hk[2]; hk[2] = hk[3]; hk[3] = 0; }
-      if (lane == j) my_key = best;
+    static_assert(MU == 2 || MU == 4, "two or four candidates per lane");
+    if constexpr (MU == 2) {
+      cx(0, 1);
+    } else {
+      cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
     }
-    // softmax, then the K weights in parallel (lane j: the j-th winner)
+    uint64_t my_key = 0;
+    double lmax = 0.0, z = 0.0;
+    float ex[MU];
+    for (int j = 0; j < K; j++) {
+      const uint32_t hi = (uint32_t)(hk[0] >> 32);
+      const uint32_t bh = wave_max_u32(hi);
+      uint64_t m = __ballot(hi == bh);
+      if (__popcll(m) != 1) {   // equal upper halves: the whole keys of those lanes decide
+        const uint64_t best = wave_max_key(hi == bh ? hk[0] : 0ull);
+        m = __ballot(hk[0] == best);
+      }
+      const int wl = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+      const uint64_t best = ((uint64_t)__builtin_amdgcn_readlane((int)(uint32_t)(hk[0] >> 32), wl) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)hk[0], wl);
+      if (lane == wl) {
+#pragma unroll
+        for (int u = 0; u + 1 < MU; u++) hk[u] = hk[u + 1];
+        hk[MU - 1] = 0;
+      }
+      if (lane == j) my_key = best;
+      if (j == 0) {
+        // the shift: the winner's logit, read from the lane that holds it
+        const int e0 = key_expert(best), u0 = e0 % MU;
+        double lu = l[0];
+#pragma unroll
+        for (int u = 1; u < MU; u++) lu = u == u0 ? l[u] : lu;
+        const uint64_t b = __builtin_bit_cast(uint64_t, lu);
+        lmax = __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), e0 / MU) << 32) |
+                                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, e0 / MU));
+        double zl = 0.0;
+#pragma unroll
+        for (int u = 0; u < MU; u++) {
+          ex[u] = MU * lane + u < E ? exp_nonpos(l[u] - lmax) : 0.f;
+          zl += (double)ex[u];
+        }
+        z = wave_sum(zl);
+      }
+    }
+    // the K weights in parallel (lane j: the j-th winner's exponential from its lane)
     const int my_e = key_expert(my_key);
-    double lmax = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < MU; u++) lmax = fmax(lmax, l[u]);
-    lmax = wave_max(lmax);
-    double z = 0.0;
-#pragma unroll
-    for (int u = 0; u < MU; u++)
-      if (u * kWave + lane < E) z += exp(l[u] - lmax);
-    z = wave_sum(z);
-    // the winner's logit: lane j reads it from the lane that holds expert my_e
-    double lw = -INFINITY;
+    float e_sel = 0.f;
 #pragma unroll
     for (int u = 0; u < MU; u++) {
-      const double v = __shfl(l[u], my_e & 63);
-      if ((my_e >> 6) == u) lw = v;
+      const float v = __shfl(ex[u], (my_e / MU) & 63);
+      if (my_e % MU == u) e_sel = v;
     }
-    double my_w = exp(lw - lmax) / z;
+    double my_w = (double)e_sel / z;
     // weights (divided by their sum over the row's k when asked), in selection order
     if (a.renorm) my_w = my_w / wave_sum(lane < K ? my_w : 0.0);
     if (lane < K) {
@@ -318,7 +358,10 @@ int launch_route(const RouteArgs& a, hipStream_t stream, const Prof* p) {
     launch(k_route_logits<true>, dim3(n_hc * n_eg), dim3(256), 0, stream, p ? &p0 : nullptr, a);
   else
     launch(k_route_logits<false>, dim3(n_hc * n_eg), dim3(256), 0, stream, p ? &p0 : nullptr, a);
-  launch(k_route_final, dim3(1), dim3(kFinalThreads), 0, stream, p ? &p1 : nullptr, a);
+  if (a.n_experts <= 2 * kWave)
+    launch(k_route_final<2>, dim3(1), dim3(kFinalThreads), 0, stream, p ? &p1 : nullptr, a);
+  else
+    launch(k_route_final<4>, dim3(1), dim3(kFinalThreads), 0, stream, p ? &p1 : nullptr, a);
   return (int)hipGetLastError();
 }
 
