@@ -62,6 +62,7 @@ def lib():
         L.oracle_moe.argtypes = [P, I, I, I, I, QP, QP, QP, QP, QP, QP, I, P, P, P, P, P]
         L.oracle_moe.restype = None
         L.oracle_head.argtypes = [P, I, I, I, QP, I, I, P, P]; L.oracle_head.restype = None
+        L.oracle_accept.argtypes = [I, I, P, P, P, P]; L.oracle_accept.restype = I
         L.oracle_threads.argtypes = []; L.oracle_threads.restype = I
         _lib = L
     return _lib
@@ -181,6 +182,20 @@ def head(x, q, v0=0, v1=None):
     logits = np.empty((R, v1 - v0)); am = np.empty(R, np.int32)
     lib().oracle_head(_p(x), _xdt(x), R, H, ctypes.byref(q), v0, v1, _p(logits), _p(am))
     return logits, am
+
+
+def accept(argmax, proposal, mtp=True):
+    """Greedy verification of a window's proposals. argmax [rows] (the head's argmax per
+    row), proposal [n_slots] (ignored without mtp). Returns (tokens [n_slots, 2] int32
+    with -1 where unused, n_tokens [n_slots] int32, number of kept proposals)."""
+    am = _c(argmax, np.int32)
+    n_slots = am.size // 2 if mtp else am.size
+    assert am.size == (2 * n_slots if mtp else n_slots)
+    prop = _c(proposal if proposal is not None else np.zeros(n_slots), np.int32)
+    tokens = np.empty((n_slots, 2), np.int32)
+    n_tok = np.empty(n_slots, np.int32)
+    kept = lib().oracle_accept(n_slots, int(bool(mtp)), _p(am), _p(prop), _p(tokens), _p(n_tok))
+    return tokens, n_tok, kept
 
 
 def threads():

@@ -313,6 +313,39 @@ void oracle_head(const void* x, int x_dtype, int R, int H, const oracle_qmat* he
   }
 }
 
+/* ------------------------------------------------------------------ verify/accept */
+
+/*
+ * Greedy verification of a window's MTP proposals (Strata docs/BATCHING.md, the
+ * --batch-mtp paragraph: each slot verifies one proposal alongside its current token, so
+ * a window carries two rows per slot; docs/MULTI_GPU.md, the --pipeline-windows
+ * paragraph: a window accepted whole also yields a bonus token).
+ *
+ * Rows: with mtp, slot s owns rows 2s (its current token) and 2s + 1 (its proposal);
+ * without, row s. argmax[r] is the model's next token after row r (the head's argmax).
+ * A slot's proposal is kept when it equals the next token after the slot's token row;
+ * the slot then emits the proposal and the next token after the proposal row (two
+ * tokens), otherwise the next token after its token row alone (one token). tokens is
+ * [n_slots][2] (-1 where unused), n_tokens [n_slots]. Returns the number of kept
+ * proposals.
+ */
+int oracle_accept(int n_slots, int mtp, const int32_t* argmax, const int32_t* proposal,
+                  int32_t* tokens, int32_t* n_tokens) {
+  int kept = 0;
+  for (int s = 0; s < n_slots; s++) {
+    const int32_t next_after_token = argmax[mtp ? 2 * s : s];
+    tokens[2 * s] = next_after_token;
+    tokens[2 * s + 1] = -1;
+    n_tokens[s] = 1;
+    if (mtp && proposal[s] == next_after_token) {
+      tokens[2 * s + 1] = argmax[2 * s + 1];
+      n_tokens[s] = 2;
+      kept++;
+    }
+  }
+  return kept;
+}
+
 /* Threads OpenMP would use for the parallel loops above (1 without OpenMP). */
 int oracle_threads(void) {
 #ifdef _OPENMP

@@ -378,3 +378,65 @@ def test_head_argmax_ties_take_lower_index(oracle_lib):
     x = np.ones((2, H), np.float32)
     _, am = oracle_lib.head(x, q)
     assert list(am) == [9, 9]
+
+
+# ---------------------------------------------------------------- verify / accept
+# Greedy verification of one MTP proposal per slot (Strata docs/BATCHING.md, --batch-mtp
+# paragraph; docs/MULTI_GPU.md, --pipeline-windows paragraph: an accepted window yields a
+# bonus token).
+
+def test_accept_hand_cases(oracle_lib):
+    # slot 0: proposal 7 == argmax of its token row -> kept, bonus 9
+    # slot 1: proposal 4 != 5 -> rejected, emits the correction 5
+    # slot 2: proposal 0 == 0 -> kept, bonus 0
+    argmax = np.array([7, 9, 5, 6, 0, 0], np.int32)
+    tokens, n_tok, kept = oracle_lib.accept(argmax, np.array([7, 4, 0], np.int32))
+    np.testing.assert_array_equal(tokens, [[7, 9], [5, -1], [0, 0]])
+    np.testing.assert_array_equal(n_tok, [2, 1, 2])
+    assert kept == 2
+
+
+def test_accept_without_mtp_emits_one_token_per_row(oracle_lib):
+    argmax = np.array([3, 1, 4, 1, 5, 9, 2, 6], np.int32)
+    tokens, n_tok, kept = oracle_lib.accept(argmax, None, mtp=False)
+    np.testing.assert_array_equal(tokens[:, 0], argmax)
+    assert (tokens[:, 1] == -1).all() and (n_tok == 1).all() and kept == 0
+
+
+def test_accept_reproduces_serial_greedy_decoding(oracle_lib):
+    """Speculative windows give the serial loop's tokens: a toy greedy model whose next
+    token is a fixed function of the current one, four slots decoding in windows with a
+    drafter that is right about two times in three, against plain one-token-at-a-time
+    greedy decoding of the same model."""
+    rng = np.random.default_rng(5)
+    V = 50
+    nxt = rng.integers(0, V, size=V)            # the model: next token after t
+
+    def serial(t0, n):
+        out, t = [], t0
+        for _ in range(n):
+            t = int(nxt[t])
+            out.append(t)
+        return out
+
+    slots = 4
+    starts = rng.integers(0, V, size=slots)
+    gen = [[] for _ in range(slots)]
+    cur = [int(s) for s in starts]
+    total_kept = total_windows = 0
+    while min(len(g) for g in gen) < 40:
+        # drafter: right with probability 2/3, otherwise a wrong token
+        prop = np.array([int(nxt[c]) if rng.random() < 2 / 3 else int((nxt[c] + 1 + rng.integers(V - 1)) % V)
+                         for c in cur], np.int32)
+        # the window's rows: (token, proposal) per slot; the model's argmax per row
+        argmax = np.array([int(nxt[v]) for c, p in zip(cur, prop) for v in (c, p)], np.int32)
+        tokens, n_tok, kept = oracle_lib.accept(argmax, prop)
+        total_kept += kept
+        total_windows += slots
+        for s in range(slots):
+            emitted = [int(t) for t in tokens[s, :n_tok[s]]]
+            gen[s].extend(emitted)
+            cur[s] = emitted[-1]
+    for s in range(slots):
+        assert gen[s] == serial(int(starts[s]), len(gen[s]))
+    assert 0.5 < total_kept / total_windows < 0.8
