@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--layers", type=int, default=16, help="layer instances to cycle through")
     p.add_argument("--windows", type=int, default=256, help="distinct activation windows")
     p.add_argument("--prof-steps", type=int, default=512, help="eager steps timed per kernel")
+    p.add_argument("--inflight", type=int, default=1,
+                   help="independent windows in flight (windows alternate over this many streams, "
+                        "like pipelined slot groups); 1 = one window after the other")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget (0: skip)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first copy this many MiB device to device three times (a dispatch of known "
@@ -101,7 +104,7 @@ def counter_traffic(kernel, workload):
 class Steps:
     """Device state of K steps: layers, windows, per-step routing outputs, workspaces."""
 
-    def __init__(self, cfg, n_layers, n_windows, steps, sw, torch, synth, DevLayer, to_dev_x):
+    def __init__(self, cfg, n_layers, n_windows, steps, sw, torch, synth, DevLayer, to_dev_x, inflight=1):
         self.cfg, self.sw, self.torch = cfg, sw, torch
         R, H, E, k = cfg.rows, cfg.hidden, cfg.experts, cfg.top_k
         t0 = time.time()
@@ -137,17 +140,21 @@ class Steps:
             for name, t in self.big.items():
                 setattr(ro, name, t[i])
             self.routes.append(ro)
-        self.ws_r = sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E))
-        self.ws_m = sw.workspace(sw.workspace_bytes(1, R, H, cfg.ffn, E, k))
-        self.out = torch.empty(R, H, dtype=torch.float32, device=dev)
+        # one set of workspaces and outputs per window in flight
+        self.ws_r = [sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E)) for _ in range(inflight)]
+        self.ws_m = [sw.workspace(sw.workspace_bytes(1, R, H, cfg.ffn, E, k)) for _ in range(inflight)]
+        self.out = [torch.empty(R, H, dtype=torch.float32, device=dev) for _ in range(inflight)]
+        self.inflight = inflight
 
     def step(self, i, prof_route=None, prof_moe=None):
         cfg, sw = self.cfg, self.sw
         dl = self.layers[i % len(self.layers)]
         x = self.xs[i % len(self.xs)]
-        ro = sw.strata_window_route(x, dl.gate_w, dl.bias, cfg.top_k, out=self.routes[i], ws=self.ws_r,
+        j = i % self.inflight
+        ro = sw.strata_window_route(x, dl.gate_w, dl.bias, cfg.top_k, out=self.routes[i], ws=self.ws_r[j],
                                     prof=prof_route)
-        sw.strata_window_moe(x, dl.gate, dl.up, dl.down, *dl.sh, ro, out=self.out, ws=self.ws_m, prof=prof_moe)
+        sw.strata_window_moe(x, dl.gate, dl.up, dl.down, *dl.sh, ro, out=self.out[j], ws=self.ws_m[j],
+                             prof=prof_moe)
 
     def distinct_experts(self, steps):
         return (self.big["n_active"][:steps, 0] - 1).cpu().numpy()
@@ -228,7 +235,8 @@ def main():
         return bench_stack(args, torch, synth, sw, DevLayer, to_dev_x)
     cfg = synth.config(args.config, **({"rows": args.rows} if args.rows else {}))
     K, W = args.steps, args.warmup
-    st = Steps(cfg, args.layers, args.windows, max(K, args.prof_steps), sw, torch, synth, DevLayer, to_dev_x)
+    NF = max(1, args.inflight)
+    st = Steps(cfg, args.layers, args.windows, max(K, args.prof_steps), sw, torch, synth, DevLayer, to_dev_x, NF)
 
     for i in range(W):
         st.step(i)
@@ -247,14 +255,22 @@ def main():
     d_dn = [evs[6 * i + 4].elapsed_time(evs[6 * i + 5]) for i in range(P)]
     U_prof = st.distinct_experts(P)
 
-    # ---- the timed region: one graph of K steps
+    # ---- the timed region: one graph of K steps (window i on stream i % inflight; the
+    # windows of one stream run one after the other)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
+    side = [torch.cuda.Stream() for _ in range(NF - 1)]
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
+            for t in side:
+                t.wait_stream(s)
+            lanes = [s] + side
             for i in range(K):
-                st.step(i)
+                with torch.cuda.stream(lanes[i % NF]):
+                    st.step(i)
+            for t in side:
+                s.wait_stream(t)
     torch.cuda.synchronize()
     g.replay()                      # warm replay
     torch.cuda.synchronize()
@@ -304,7 +320,8 @@ def main():
         "ms_per_step": round(ms_total / K, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": workload, "config_id": cfg.cid, "rows": R, "hidden": H, "ffn": F, "experts": E,
-                   "top_k": cfg.top_k, "bits": cfg.bits, "layer_instances": args.layers},
+                   "top_k": cfg.top_k, "bits": cfg.bits, "layer_instances": args.layers,
+                   "windows_in_flight": NF},
         "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "mean_distinct_experts": round(float(U.mean()), 2),
         "unique_weight_bytes_per_window": round(bytes_total / K),
