@@ -189,6 +189,27 @@ int strata_window_head(void* stream, const void* x, int x_dtype, int rows, int h
                        const strata_qmat* head, int vocab, float* logits,
                        int32_t* argmax, void* ws, size_t ws_bytes, void* const* prof_events);
 
+/*
+ * strata_window_accept - greedy verification of the window's MTP proposals (Strata
+ * docs/BATCHING.md, the --batch-mtp paragraph: each slot verifies one proposal beside its
+ * current token, two rows per slot; docs/MULTI_GPU.md, the --pipeline-windows paragraph:
+ * a window accepted whole also yields a bonus token).
+ *   argmax   [rows] int32: the head's argmax per row (strata_window_head)
+ *   mtp = 1: slot s owns rows 2s (its current token) and 2s + 1 (its proposal), so
+ *            rows == 2 * n_slots; proposal [n_slots] int32 is the token each proposal row
+ *            carries. The proposal is kept when it equals argmax[2s]; the slot then emits
+ *            tokens[s] = {proposal, argmax[2s + 1]} (n_tokens 2), else
+ *            {argmax[2s], -1} (n_tokens 1).
+ *   mtp = 0: rows == n_slots, proposal may be NULL; slot s emits {argmax[s], -1}.
+ *   tokens [n_slots][2] int32, n_tokens [n_slots] int32, n_accepted [1] int32 (the kept
+ *   proposals of the window): outputs.
+ * Errors: STRATA_EINVAL for mtp not 0/1, n_slots outside 1..8/(mtp ? 2 : 1), rows not
+ * matching, or a NULL / misaligned pointer. One wave; no workspace.
+ */
+int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_slots, int mtp,
+                         const int32_t* proposal, int32_t* tokens, int32_t* n_tokens,
+                         int32_t* n_accepted, void* const* prof_events);
+
 /* Workspace bytes for which = 0 (route), 1 (moe), 2 (head); 0 for invalid arguments. */
 size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts,
                                int top_k, int vocab);

@@ -159,3 +159,19 @@ def test_window_limits_from_pages(sw):
     # the synthetic workloads: two MTP slots = 4 rows, four MTP slots = 8 rows
     assert synth.config(1).rows == 2 * g["rows_per_slot_with_batch_mtp"] == g["workloads"]["two_slots_mtp"]
     assert synth.config(2).rows == 4 * g["rows_per_slot_with_batch_mtp"] == g["workloads"]["four_slots_mtp"]
+
+
+def test_accept_rejects(sw):
+    L = sw.library()
+    def call(rows=8, n_slots=4, mtp=1, am=A, prop=A, tok=A, ntok=A, nacc=A):
+        return L.strata_window_accept(None, am, rows, n_slots, mtp, prop, tok, ntok, nacc, None)
+    assert call(mtp=2) == sw.STRATA_EINVAL
+    assert call(n_slots=5, rows=10) == sw.STRATA_EINVAL          # more than 8 rows with MTP
+    assert call(n_slots=0, rows=0) == sw.STRATA_EINVAL
+    assert call(rows=7) == sw.STRATA_EINVAL                      # not two rows per slot
+    assert call(mtp=0, n_slots=4, rows=8) == sw.STRATA_EINVAL   # one row per slot without MTP
+    assert call(mtp=0, n_slots=9, rows=9) == sw.STRATA_EINVAL
+    assert call(prop=None) == sw.STRATA_EINVAL                   # MTP needs the proposals
+    assert call(am=None) == sw.STRATA_EINVAL
+    assert call(tok=A + 4) == sw.STRATA_EINVAL
+    assert call(nacc=0) == sw.STRATA_EINVAL

@@ -56,6 +56,8 @@ def library():
         L.strata_window_moe.restype = I
         L.strata_window_head.argtypes = [P, P, I, I, I, ctypes.POINTER(CQMat), I, P, P, P, S, P]
         L.strata_window_head.restype = I
+        L.strata_window_accept.argtypes = [P, P, I, I, I, P, P, P, P, P]
+        L.strata_window_accept.restype = I
         L.strata_window_workspace.argtypes = [I, I, I, I, I, I, I]
         L.strata_window_workspace.restype = S
         L.strata_window_last_error.argtypes = []
@@ -238,3 +240,27 @@ def strata_window_head(x, head, logits=True, argmax=None, ws=None, stream=None, 
     _check(library().strata_window_head(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ctypes.byref(q),
                                         V, _ptr(lg), _ptr(am), _ptr(ws), ws.numel(), _events(prof)))
     return lg, am[:rows]
+
+
+def strata_window_accept(argmax, proposal=None, mtp=True, tokens=None, n_tokens=None, n_accepted=None,
+                         stream=None, prof=None):
+    """Greedy verification of the window's MTP proposals (see strata_window_accept).
+    argmax: int32 [rows]; proposal: int32 [rows // 2] with mtp. Returns (tokens [n_slots, 2],
+    n_tokens [n_slots], n_accepted [1]) int32 device tensors."""
+    _need(argmax, "argmax")
+    if argmax.dtype != torch.int32:
+        raise TypeError("argmax must be int32")
+    rows = argmax.numel()
+    n_slots = rows // 2 if mtp else rows
+    if mtp:
+        _need(proposal, "proposal")
+        if proposal.dtype != torch.int32:
+            raise TypeError("proposal must be int32")
+    i32 = dict(dtype=torch.int32, device=argmax.device)
+    tokens = torch.empty(n_slots, 2, **i32) if tokens is None else tokens
+    n_tokens = torch.empty(n_slots, **i32) if n_tokens is None else n_tokens
+    n_accepted = torch.empty(4, **i32) if n_accepted is None else n_accepted
+    _check(library().strata_window_accept(_stream(stream), _ptr(argmax), rows, n_slots, int(bool(mtp)),
+                                          _ptr(proposal) if mtp else None, _ptr(tokens), _ptr(n_tokens),
+                                          _ptr(n_accepted), _events(prof)))
+    return tokens, n_tokens, n_accepted

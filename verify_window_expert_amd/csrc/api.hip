@@ -264,4 +264,26 @@ int strata_window_head(void* stream, const void* x, int x_dtype, int rows, int h
   return launch_status(sw::launch_head(a, (hipStream_t)stream, prof_events ? &ph : nullptr), "head");
 }
 
+int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_slots, int mtp,
+                         const int32_t* proposal, int32_t* tokens, int32_t* n_tokens, int32_t* n_accepted,
+                         void* const* prof_events) {
+  g_err[0] = 0;
+  if (mtp != 0 && mtp != 1) return fail(STRATA_EINVAL, "mtp %d is neither 0 nor 1", mtp);
+  if (n_slots < 1 || n_slots > STRATA_MAX_ROWS / (mtp ? 2 : 1))
+    return fail(STRATA_EINVAL, "n_slots %d outside 1..%d", n_slots, STRATA_MAX_ROWS / (mtp ? 2 : 1));
+  if (rows != n_slots * (mtp ? 2 : 1))
+    return fail(STRATA_EINVAL, "rows %d is not %d per slot x %d slots", rows, mtp ? 2 : 1, n_slots);
+  const void* p[] = {argmax, tokens, n_tokens, n_accepted};
+  const char* nm[] = {"argmax", "tokens", "n_tokens", "n_accepted"};
+  for (int i = 0; i < 4; i++)
+    if (!p[i] || !aligned(p[i], 16)) return fail(STRATA_EINVAL, "%s NULL or not 16-byte aligned", nm[i]);
+  if (mtp && (!proposal || !aligned(proposal, 16)))
+    return fail(STRATA_EINVAL, "proposal NULL or not 16-byte aligned");
+  sw::AcceptArgs a;
+  a.argmax = argmax; a.n_slots = n_slots; a.mtp = mtp; a.proposal = proposal;
+  a.tokens = tokens; a.n_tokens = n_tokens; a.n_accepted = n_accepted;
+  const sw::Prof pa = prof(prof_events, 0);
+  return launch_status(sw::launch_accept(a, (hipStream_t)stream, prof_events ? &pa : nullptr), "accept");
+}
+
 }  // extern "C"

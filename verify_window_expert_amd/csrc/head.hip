@@ -188,6 +188,35 @@ __global__ __launch_bounds__(kHeadThreads) void k_head_argmax(HeadArgs a, int nw
   }
 }
 
+// Greedy verification of the window's proposals (Strata docs/BATCHING.md, --batch-mtp
+// paragraph; docs/MULTI_GPU.md, --pipeline-windows paragraph): one wave, lane s = slot s.
+// With mtp, slot s owns rows 2s (its token) and 2s + 1 (its proposal). The proposal is
+// kept when it equals the head's argmax of the token row; the slot then emits it and
+// the argmax of the proposal row, else the token row's argmax alone.
+__global__ __launch_bounds__(kWave) void k_accept(AcceptArgs a) {
+  const int s = threadIdx.x;
+  bool kept = false;
+  if (s < a.n_slots) {
+    const int32_t first = a.argmax[a.mtp ? 2 * s : s];
+    int32_t second = -1;
+    if (a.mtp) {
+      const int32_t prop = a.proposal[s], bonus = a.argmax[2 * s + 1];
+      kept = prop == first;
+      if (kept) second = bonus;
+    }
+    a.tokens[2 * s] = first;
+    a.tokens[2 * s + 1] = second;
+    a.n_tokens[s] = kept ? 2 : 1;
+  }
+  const uint64_t b = __ballot(kept);
+  if (s == 0) *a.n_accepted = (int32_t)__popcll(b);
+}
+
+int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p) {
+  launch(k_accept, dim3(1), dim3(kWave), 0, s, p, a);
+  return (int)hipGetLastError();
+}
+
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p) {
   const size_t lds = head_lds_bytes(a.hidden, a.x_dtype == 0 ? 16 : 8);
   static size_t granted = 64 * 1024;   // raise the dynamic LDS limit once, when needed

@@ -54,6 +54,12 @@ struct HeadArgs {
   float* part_val; int32_t* part_idx;   // [workgroups][rows]
 };
 
+struct AcceptArgs {
+  const int32_t* argmax; int n_slots, mtp;
+  const int32_t* proposal;  // [n_slots] (mtp only)
+  int32_t* tokens; int32_t* n_tokens; int32_t* n_accepted;
+};
+
 // Optional timing events of one launch (both may be null): recorded by the dispatch
 // itself at the kernel's start and end (hipExtLaunchKernel).
 struct Prof {
@@ -74,6 +80,7 @@ int launch_route(const RouteArgs& a, hipStream_t s, const Prof* p);
 int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
 int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
+int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
 int head_workgroups(int vocab);
 int down_ranges(int hidden);
 // dynamic LDS of the gate/up and down kernels (the activation image)
