@@ -63,6 +63,8 @@ def lib():
         L.oracle_moe.restype = None
         L.oracle_head.argtypes = [P, I, I, I, QP, I, I, P, P]; L.oracle_head.restype = None
         L.oracle_accept.argtypes = [I, I, P, P, P, P]; L.oracle_accept.restype = I
+        L.oracle_tier_count.argtypes = [I, P, P, ctypes.c_float]; L.oracle_tier_count.restype = None
+        L.oracle_tier_select.argtypes = [I, P, P, I, ctypes.c_float, P]; L.oracle_tier_select.restype = I
         L.oracle_threads.argtypes = []; L.oracle_threads.restype = I
         _lib = L
     return _lib
@@ -196,6 +198,26 @@ def accept(argmax, proposal, mtp=True):
     n_tok = np.empty(n_slots, np.int32)
     kept = lib().oracle_accept(n_slots, int(bool(mtp)), _p(am), _p(prop), _p(tokens), _p(n_tok))
     return tokens, n_tok, kept
+
+
+def tier_count(row_mask, counts, decay):
+    """One window's routing counts: counts[e] = fmaf(counts[e], decay, rows routed to e)
+    for the routed experts (row_mask [E+1] uint8; the shared expert's entry is not
+    counted). Returns the new float32 counts [E]."""
+    rm = _c(row_mask, np.uint8)
+    c = np.array(counts, np.float32, copy=True)
+    lib().oracle_tier_count(c.size, _p(rm), _p(c), float(decay))
+    return c
+
+
+def tier_select(counts, resident, max_swaps, min_gain=1.5):
+    """One round of the adaptive tier. Returns (new resident [E] uint8, swaps [n, 2] int32
+    as (in, out) pairs)."""
+    c = _c(counts, np.float32)
+    res = np.array(resident, np.uint8, copy=True)
+    sw = np.empty(2 * max(max_swaps, 1), np.int32)
+    n = lib().oracle_tier_select(c.size, _p(c), _p(res), int(max_swaps), float(min_gain), _p(sw))
+    return res, sw[:2 * n].reshape(n, 2)
 
 
 def threads():

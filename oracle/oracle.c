@@ -346,6 +346,76 @@ int oracle_accept(int n_slots, int mtp, const int32_t* argmax, const int32_t* pr
   return kept;
 }
 
+/* ---------------------------------------------------------- routing counts and tier */
+
+/*
+ * Expert routing counts and the adaptive tier's swap choice (Strata docs/BATCHING.md,
+ * the paragraph on batch windows counting the experts they route to: every
+ * --adapt-every windows the engine swaps the most-routed experts that are not in the fast
+ * tier in for the least-routed resident ones; --adapt-decay applies; --adapt-min-gain F
+ * (default 1.5) is the bar a swap must clear, the incoming expert's count against the
+ * outgoing one's).
+ *
+ * Readings where the pages leave the step open: a window adds, for each routed expert e,
+ * the number of its rows that route to e (row_mask[e]'s bits), after scaling the running
+ * count by decay: counts[e] = fmaf(counts[e], decay, rows_e), in float (the same
+ * precision on every side, since the comparisons below decide integers).
+ */
+void oracle_tier_count(int E, const uint8_t* row_mask, float* counts, float decay) {
+  for (int e = 0; e < E; e++) {
+    int n = 0;
+    for (int r = 0; r < 8; r++) n += (row_mask[e] >> r) & 1;
+    counts[e] = fmaf(counts[e], decay, (float)n);
+  }
+}
+
+typedef struct { float c; int e; } tier_key;
+static int by_count_desc(const void* a, const void* b) {
+  const tier_key *x = a, *y = b;
+  if (x->c != y->c) return x->c > y->c ? -1 : 1;
+  return x->e - y->e;
+}
+static int by_count_asc(const void* a, const void* b) {
+  const tier_key *x = a, *y = b;
+  if (x->c != y->c) return x->c < y->c ? -1 : 1;
+  return x->e - y->e;
+}
+
+/*
+ * The swap choice of one round: the experts outside the tier ordered by count, largest
+ * first, and the resident ones ordered by count, smallest first (ties: the lower expert
+ * index first, in both lists); pair i swaps in_i for out_i while in_i's count is positive
+ * and at least min_gain * out_i's count (the product in float), for at most max_swaps
+ * pairs. resident[] is updated; swaps receives (in, out) pairs. Returns the swap count.
+ */
+int oracle_tier_select(int E, const float* counts, uint8_t* resident, int max_swaps, float min_gain,
+                       int32_t* swaps) {
+  tier_key* in = malloc(sizeof(tier_key) * (E > 0 ? E : 1));
+  tier_key* out = malloc(sizeof(tier_key) * (E > 0 ? E : 1));
+  int n_in = 0, n_out = 0;
+  for (int e = 0; e < E; e++) {
+    tier_key k = {counts[e], e};
+    if (resident[e]) out[n_out++] = k; else in[n_in++] = k;
+  }
+  qsort(in, n_in, sizeof(tier_key), by_count_desc);
+  qsort(out, n_out, sizeof(tier_key), by_count_asc);
+  int n = 0;
+  while (n < max_swaps && n < n_in && n < n_out) {
+    const float bar = min_gain * out[n].c;
+    if (!(in[n].c > 0.0f && in[n].c >= bar)) break;
+    swaps[2 * n] = in[n].e;
+    swaps[2 * n + 1] = out[n].e;
+    n++;
+  }
+  for (int i = 0; i < n; i++) {
+    resident[swaps[2 * i]] = 1;
+    resident[swaps[2 * i + 1]] = 0;
+  }
+  free(in);
+  free(out);
+  return n;
+}
+
 /* Threads OpenMP would use for the parallel loops above (1 without OpenMP). */
 int oracle_threads(void) {
 #ifdef _OPENMP

@@ -440,3 +440,63 @@ def test_accept_reproduces_serial_greedy_decoding(oracle_lib):
     for s in range(slots):
         assert gen[s] == serial(int(starts[s]), len(gen[s]))
     assert 0.5 < total_kept / total_windows < 0.8
+
+
+# ------------------------------------------------------- routing counts and the tier
+# Strata docs/BATCHING.md: batch windows count the experts they route to; every
+# --adapt-every windows the most-routed experts outside the fast tier are swapped in for
+# the least-routed resident ones, each swap clearing --adapt-min-gain (default 1.5).
+
+def test_tier_count_matches_bruteforce_and_decay_closed_form(oracle_lib):
+    rng = np.random.default_rng(3)
+    E, R = 64, 8
+    c = np.zeros(E, np.float32)
+    hist = np.zeros(E)
+    for w in range(6):
+        idx = np.stack([rng.choice(E, 8, replace=False) for _ in range(R)])
+        mask = np.zeros(E + 1, np.uint8)
+        for r in range(R):
+            for e in idx[r]:
+                mask[e] |= 1 << r
+        mask[E] = 0xFF                                   # the shared expert: not counted
+        c = oracle_lib.tier_count(mask, c, 0.5)
+        hist = hist * 0.5 + np.bincount(idx.ravel(), minlength=E)   # closed form, exact in binary
+    np.testing.assert_array_equal(c, hist.astype(np.float32))
+
+
+def test_tier_select_hand_case(oracle_lib):
+    counts = np.array([9, 0, 4, 6, 1, 3, 2, 5], np.float32)
+    resident = np.array([0, 1, 0, 1, 1, 0, 1, 0], np.uint8)
+    # outside, by count: 0 (9), 7 (5), 2 (4), 5 (3); resident, ascending: 1 (0), 4 (1), 6 (2), 3 (6)
+    # pairs: 9 vs 0 ok, 5 vs 1 ok, 4 vs 2 ok (4 >= 3), 3 vs 6 fails
+    res, sw = oracle_lib.tier_select(counts, resident, max_swaps=8, min_gain=1.5)
+    np.testing.assert_array_equal(sw, [[0, 1], [7, 4], [2, 6]])
+    np.testing.assert_array_equal(res, [1, 0, 1, 1, 0, 0, 0, 1])
+    _, sw2 = oracle_lib.tier_select(counts, resident, max_swaps=2, min_gain=1.5)
+    np.testing.assert_array_equal(sw2, [[0, 1], [7, 4]])
+    _, sw3 = oracle_lib.tier_select(counts, resident, max_swaps=8, min_gain=2.5)   # 4 < 2.5 * 2
+    np.testing.assert_array_equal(sw3, [[0, 1], [7, 4]])
+
+
+def test_tier_select_bruteforce_properties(oracle_lib):
+    """Against an exhaustive definition: the swaps are the longest prefix of the paired
+    orderings that clears the bar, and no expert moves twice."""
+    rng = np.random.default_rng(11)
+    for trial in range(50):
+        E = int(rng.integers(4, 40))
+        counts = rng.integers(0, 6, size=E).astype(np.float32) * np.float32(0.75)
+        resident = (rng.random(E) < 0.5).astype(np.uint8)
+        gain = np.float32(rng.choice([1.0, 1.5, 2.0]))
+        ms = int(rng.integers(1, 10))
+        res, sw = oracle_lib.tier_select(counts, resident, max_swaps=ms, min_gain=gain)
+        ins = sorted([e for e in range(E) if not resident[e]], key=lambda e: (-counts[e], e))
+        outs = sorted([e for e in range(E) if resident[e]], key=lambda e: (counts[e], e))
+        for i, (a, b) in enumerate(sw):
+            assert a == ins[i] and b == outs[i]
+            assert counts[a] > 0 and counts[a] >= np.float32(gain * counts[b])
+        n = len(sw)
+        if n < min(ms, len(ins), len(outs)):   # the next pair fails the bar
+            a, b = ins[n], outs[n]
+            assert not (counts[a] > 0 and counts[a] >= np.float32(gain * counts[b]))
+        assert res.sum() == resident.sum()
+        assert len(set(sw.ravel())) == 2 * n
