@@ -210,6 +210,31 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
                          const int32_t* proposal, int32_t* tokens, int32_t* n_tokens,
                          int32_t* n_accepted, void* const* prof_events);
 
+/*
+ * strata_window_tier - routing counts of the window and the adaptive tier's swap choice
+ * (Strata docs/BATCHING.md, the paragraph on batch windows counting the experts they
+ * route to: every --adapt-every windows the most-routed experts outside the fast tier are
+ * swapped in for the least-routed resident ones; --adapt-decay; --adapt-min-gain F, the
+ * bar a swap clears: the incoming expert's count against the outgoing one's).
+ *   row_mask [n_experts + 1] uint8: strata_route_out.row_mask of the window (the shared
+ *            expert's entry is not counted)
+ *   counts   [n_experts] float, in/out: counts[e] = fmaf(counts[e], decay, number of the
+ *            window's rows routed to e); decay in [0, 1]
+ *   resident NULL: counting only. Else [n_experts] uint8 in/out (nonzero = in the fast
+ *            tier) and a selection round follows the count: the experts outside the tier
+ *            by count, largest first, are paired with the resident ones by count,
+ *            smallest first (ties: lower expert index first in both); pair i swaps while
+ *            every pair up to it has an incoming count > 0 and >= min_gain * outgoing
+ *            count (product in float), at most max_swaps pairs.
+ *   swaps    [2 * max_swaps] int32 out: (in, out) expert pairs; n_swaps [1] int32 out.
+ * Errors: STRATA_EINVAL for n_experts outside 1..256, decay outside [0, 1], max_swaps
+ * outside 0..n_experts, a negative or non-finite min_gain, or a NULL / misaligned pointer.
+ * One workgroup; no workspace.
+ */
+int strata_window_tier(void* stream, const uint8_t* row_mask, int n_experts, float* counts, float decay,
+                       uint8_t* resident, int max_swaps, float min_gain, int32_t* swaps,
+                       int32_t* n_swaps, void* const* prof_events);
+
 /* Workspace bytes for which = 0 (route), 1 (moe), 2 (head); 0 for invalid arguments. */
 size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts,
                                int top_k, int vocab);

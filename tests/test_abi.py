@@ -175,3 +175,21 @@ def test_accept_rejects(sw):
     assert call(am=None) == sw.STRATA_EINVAL
     assert call(tok=A + 4) == sw.STRATA_EINVAL
     assert call(nacc=0) == sw.STRATA_EINVAL
+
+
+def test_tier_rejects(sw):
+    L = sw.library()
+    def call(E=128, rm=A, c=A, decay=1.0, res=A, ms=4, gain=1.5, swp=A, ns=A):
+        return L.strata_window_tier(None, rm, E, c, decay, res, ms, gain, swp, ns, None)
+    assert call(E=0) == sw.STRATA_EINVAL
+    assert call(E=257) == sw.STRATA_EINVAL
+    assert call(rm=None) == sw.STRATA_EINVAL
+    assert call(c=A + 4) == sw.STRATA_EINVAL
+    assert call(decay=1.5) == sw.STRATA_EINVAL
+    assert call(decay=float("nan")) == sw.STRATA_EINVAL
+    assert call(ms=-1) == sw.STRATA_EINVAL
+    assert call(ms=129) == sw.STRATA_EINVAL
+    assert call(gain=-1.0) == sw.STRATA_EINVAL
+    assert call(gain=float("inf")) == sw.STRATA_EINVAL
+    assert call(swp=None) == sw.STRATA_EINVAL
+    assert call(ns=None) == sw.STRATA_EINVAL

@@ -58,6 +58,8 @@ def library():
         L.strata_window_head.restype = I
         L.strata_window_accept.argtypes = [P, P, I, I, I, P, P, P, P, P]
         L.strata_window_accept.restype = I
+        L.strata_window_tier.argtypes = [P, P, I, P, ctypes.c_float, P, I, ctypes.c_float, P, P, P]
+        L.strata_window_tier.restype = I
         L.strata_window_workspace.argtypes = [I, I, I, I, I, I, I]
         L.strata_window_workspace.restype = S
         L.strata_window_last_error.argtypes = []
@@ -264,3 +266,24 @@ def strata_window_accept(argmax, proposal=None, mtp=True, tokens=None, n_tokens=
                                           _ptr(proposal) if mtp else None, _ptr(tokens), _ptr(n_tokens),
                                           _ptr(n_accepted), _events(prof)))
     return tokens, n_tokens, n_accepted
+
+
+def strata_window_tier(row_mask, counts, decay=1.0, resident=None, max_swaps=0, min_gain=1.5, swaps=None,
+                       n_swaps=None, stream=None, prof=None):
+    """Routing counts of a window (row_mask: uint8 [E + 1], e.g. RouteOut.row_mask; counts:
+    float32 [E], updated in place) and, when resident (uint8 [E], updated in place) is
+    given, one round of the adaptive tier. Returns (swaps [max_swaps, 2], n_swaps [1])
+    int32 device tensors, or None when only counting."""
+    _need(row_mask, "row_mask"); _need(counts, "counts")
+    E = counts.numel()
+    if counts.dtype != torch.float32 or row_mask.dtype != torch.uint8 or row_mask.numel() < E:
+        raise TypeError("counts must be float32 [E] and row_mask uint8 [E + 1]")
+    if resident is not None:
+        _need(resident, "resident")
+        i32 = dict(dtype=torch.int32, device=counts.device)
+        swaps = torch.empty(max(max_swaps, 1), 2, **i32) if swaps is None else swaps
+        n_swaps = torch.empty(4, **i32) if n_swaps is None else n_swaps
+    _check(library().strata_window_tier(_stream(stream), _ptr(row_mask), E, _ptr(counts), float(decay),
+                                        _ptr(resident), int(max_swaps), float(min_gain), _ptr(swaps),
+                                        _ptr(n_swaps), _events(prof)))
+    return None if resident is None else (swaps, n_swaps)

@@ -286,4 +286,28 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
   return launch_status(sw::launch_accept(a, (hipStream_t)stream, prof_events ? &pa : nullptr), "accept");
 }
 
+int strata_window_tier(void* stream, const uint8_t* row_mask, int n_experts, float* counts, float decay,
+                       uint8_t* resident, int max_swaps, float min_gain, int32_t* swaps, int32_t* n_swaps,
+                       void* const* prof_events) {
+  g_err[0] = 0;
+  if (n_experts < 1 || n_experts > STRATA_MAX_EXPERTS)
+    return fail(STRATA_EINVAL, "n_experts %d outside 1..%d", n_experts, STRATA_MAX_EXPERTS);
+  if (!row_mask || !aligned(row_mask, 16)) return fail(STRATA_EINVAL, "row_mask NULL or not 16-byte aligned");
+  if (!counts || !aligned(counts, 16)) return fail(STRATA_EINVAL, "counts NULL or not 16-byte aligned");
+  if (!(decay >= 0.f && decay <= 1.f)) return fail(STRATA_EINVAL, "decay %g outside [0, 1]", (double)decay);
+  if (resident) {
+    if (!aligned(resident, 16)) return fail(STRATA_EINVAL, "resident not 16-byte aligned");
+    if (max_swaps < 0 || max_swaps > n_experts) return fail(STRATA_EINVAL, "max_swaps %d outside 0..%d", max_swaps, n_experts);
+    if (!(min_gain >= 0.f && min_gain < 1e30f)) return fail(STRATA_EINVAL, "min_gain %g is not a finite value >= 0", (double)min_gain);
+    if (!n_swaps || !aligned(n_swaps, 16)) return fail(STRATA_EINVAL, "n_swaps NULL or not 16-byte aligned");
+    if (max_swaps > 0 && (!swaps || !aligned(swaps, 16))) return fail(STRATA_EINVAL, "swaps NULL or not 16-byte aligned");
+  }
+  sw::TierArgs a;
+  a.row_mask = row_mask; a.n_experts = n_experts; a.counts = counts; a.decay = decay;
+  a.resident = resident; a.max_swaps = resident ? max_swaps : 0; a.min_gain = min_gain;
+  a.swaps = swaps; a.n_swaps = n_swaps;
+  const sw::Prof pt = prof(prof_events, 0);
+  return launch_status(sw::launch_tier(a, (hipStream_t)stream, prof_events ? &pt : nullptr), "tier");
+}
+
 }  // extern "C"

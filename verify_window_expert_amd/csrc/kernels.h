@@ -60,6 +60,14 @@ struct AcceptArgs {
   int32_t* tokens; int32_t* n_tokens; int32_t* n_accepted;
 };
 
+struct TierArgs {
+  const uint8_t* row_mask; int n_experts;
+  float* counts; float decay;
+  uint8_t* resident;        // NULL: counting only
+  int max_swaps; float min_gain;
+  int32_t* swaps; int32_t* n_swaps;
+};
+
 // Optional timing events of one launch (both may be null): recorded by the dispatch
 // itself at the kernel's start and end (hipExtLaunchKernel).
 struct Prof {
@@ -81,6 +89,7 @@ int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof*
 int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
+int launch_tier(const TierArgs& a, hipStream_t s, const Prof* p);
 int head_workgroups(int vocab);
 int down_ranges(int hidden);
 // dynamic LDS of the gate/up and down kernels (the activation image)

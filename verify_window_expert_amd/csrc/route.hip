@@ -349,6 +349,70 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
   }
 }
 
+// ---------------------------------------------------------- routing counts and tier
+// Strata docs/BATCHING.md, the paragraph on batch windows counting the experts they route
+// to: every --adapt-every windows the most-routed experts outside the fast tier are
+// swapped in for the least-routed resident ones, each swap clearing --adapt-min-gain (the
+// incoming count against the outgoing one). One workgroup, thread e = expert e:
+//   counts[e] = fmaf(counts[e], decay, rows of the window routed to e)   (float)
+// and, on a selection round, each expert's rank in its list (outside the tier: count
+// descending; resident: ascending; ties to the lower index), then pair i = (i-th
+// outside, i-th resident) swaps while every pair up to it clears the bar.
+constexpr int kTierThreads = kMaxExpertsRoute;
+
+__global__ __launch_bounds__(kTierThreads) void k_tier(TierArgs a) {
+  __shared__ float s_c[kTierThreads];
+  __shared__ uint8_t s_res[kTierThreads];
+  __shared__ int s_in[kTierThreads], s_out[kTierThreads];
+  __shared__ int s_n[2], s_fail;
+  const int E = a.n_experts, e = threadIdx.x;
+  float c = 0.f;
+  uint8_t res = 2;   // 2: no expert
+  if (e < E) {
+    c = fmaf(a.counts[e], a.decay, (float)__builtin_popcount((uint32_t)a.row_mask[e]));
+    a.counts[e] = c;
+    if (a.resident) res = a.resident[e] ? 1 : 0;
+  }
+  if (!a.resident) return;
+  s_c[e] = c;
+  s_res[e] = res;
+  if (e < 2) s_n[e] = 0;
+  if (e == 0) s_fail = kTierThreads;
+  __syncthreads();
+  if (res != 2) {
+    int rank = 0;
+    for (int j = 0; j < E; j++) {
+      const float cj = s_c[j];
+      if (s_res[j] != res) continue;
+      rank += res ? (cj < c || (cj == c && j < e)) : (cj > c || (cj == c && j < e));
+    }
+    if (res) s_out[rank] = e; else s_in[rank] = e;
+    atomicAdd(&s_n[res], 1);
+  }
+  __syncthreads();
+  const int limit = min(a.max_swaps, min(s_n[0], s_n[1]));
+  if (e < limit) {
+    const float ci = s_c[s_in[e]], co = s_c[s_out[e]];
+    const float bar = a.min_gain * co;
+    if (!(ci > 0.f && ci >= bar)) atomicMin(&s_fail, e);
+  }
+  __syncthreads();
+  const int n = min(limit, s_fail);
+  if (e < n) {
+    const int ein = s_in[e], eout = s_out[e];
+    a.swaps[2 * e] = ein;
+    a.swaps[2 * e + 1] = eout;
+    a.resident[ein] = 1;
+    a.resident[eout] = 0;
+  }
+  if (e == 0) *a.n_swaps = n;
+}
+
+int launch_tier(const TierArgs& a, hipStream_t s, const Prof* p) {
+  launch(k_tier, dim3(1), dim3(kTierThreads), 0, s, p, a);
+  return (int)hipGetLastError();
+}
+
 int launch_route(const RouteArgs& a, hipStream_t stream, const Prof* p) {
   const int n_hc = (a.hidden + kRouteChunk - 1) / kRouteChunk;
   const int n_eg = (a.n_experts + kRouteWaves - 1) / kRouteWaves;
