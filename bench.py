@@ -190,6 +190,34 @@ def events(torch, n):
     return evs
 
 
+def window_tail_kernels(torch, sw, st, cfg, P):
+    """Average durations (us, events recorded by the dispatches) of the window's small
+    steps after the layer: the greedy verify/accept of the slots' proposals (rows as
+    token/proposal pairs, argmax and proposals synthetic) and the routing counts of the
+    adaptive tier (count-only windows and selection rounds), from the steps' routing."""
+    R, E = cfg.rows, cfg.experts
+    g = torch.Generator(device="cpu").manual_seed(7)
+    argmax = torch.randint(0, 151936, (R,), generator=g, dtype=torch.int32).cuda()
+    prop = argmax[0::2].clone()
+    prop[1::2] += 1                         # half the proposals kept
+    counts = torch.zeros(E, dtype=torch.float32, device="cuda")
+    resident = (torch.arange(E) % 3 == 0).to(torch.uint8).cuda()
+    tok, ntok, nacc = sw.strata_window_accept(argmax, prop)
+    out = {}
+    for name, fn in (("accept", lambda i, ev: sw.strata_window_accept(argmax, prop, tokens=tok, n_tokens=ntok,
+                                                                      n_accepted=nacc, prof=ev)),
+                     ("tier_count", lambda i, ev: sw.strata_window_tier(st.routes[i].row_mask, counts, 0.875,
+                                                                        prof=ev)),
+                     ("tier_select", lambda i, ev: sw.strata_window_tier(st.routes[i].row_mask, counts, 0.875,
+                                                                         resident, 8, 1.5, prof=ev))):
+        evs = events(torch, 2 * P)
+        for i in range(P):
+            fn(i, [evs[2 * i].cuda_event, evs[2 * i + 1].cuda_event])
+        torch.cuda.synchronize()
+        out[name] = round(1e3 * sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(P)) / P, 3)
+    return out
+
+
 def cpu_baseline(cfg, host_layer, seconds):
     """The CPU oracle, as it stands, on windows of the same workload until `seconds` pass."""
     import oracle
@@ -254,6 +282,7 @@ def main():
     d_gu = [evs[6 * i + 2].elapsed_time(evs[6 * i + 3]) for i in range(P)]
     d_dn = [evs[6 * i + 4].elapsed_time(evs[6 * i + 5]) for i in range(P)]
     U_prof = st.distinct_experts(P)
+    d_post = window_tail_kernels(torch, sw, st, cfg, P)
 
     # ---- the timed region: one graph of K steps (window i on stream i % inflight; the
     # windows of one stream run one after the other)
@@ -325,8 +354,8 @@ def main():
         "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "mean_distinct_experts": round(float(U.mean()), 2),
         "unique_weight_bytes_per_window": round(bytes_total / K),
-        "kernel_us": {"route": round(1e3 * sum(d_route) / P, 3), "gateup": round(1e3 * sum(d_gu) / P, 3),
-                      "down": round(1e3 * sum(d_dn) / P, 3)},
+        "kernel_us": dict({"route": round(1e3 * sum(d_route) / P, 3), "gateup": round(1e3 * sum(d_gu) / P, 3),
+                           "down": round(1e3 * sum(d_dn) / P, 3)}, **d_post),
         "wall_s": round(wall, 4),
         "roofline": roof, "cpu_baseline": cpu,
     }

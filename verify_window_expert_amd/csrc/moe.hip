@@ -167,6 +167,29 @@ __device__ __forceinline__ void load_groups(u32x4 (&xr)[XG][F32SRC ? 2 : 1], con
   }
 }
 
+// bf16 source: the values are already the hi part (lo = 0), so the permuted words are
+// byte permutes of the loaded words (input i of the group in half i % 2 of word i / 2),
+// and the block sum adds the same values in the same order as stage_group.
+__device__ __forceinline__ void stage_group_bf16(const ActLds& l, bool ok, int j, int u, const u32x4& w) {
+  u32x4 ph;
+  ph[0] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);   // inputs 0, 4
+  ph[1] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);   // inputs 1, 5
+  ph[2] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);   // inputs 2, 6
+  ph[3] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);   // inputs 3, 7
+  float shi = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const uint32_t word = w[e >> 1];
+    shi += __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+  }
+  shi += __shfl_xor(shi, 1);
+  shi += __shfl_xor(shi, 2);
+  if (ok) {
+    *(u32x4*)(l.xs + (size_t)j * l.stride + 8 * u) = ph;
+    if ((u & 3) == 0) l.sx[(u >> 2) * 16 + j] = shi;
+  }
+}
+
 template <int THREADS, int XG, bool F32SRC>
 __device__ __forceinline__ void stage_groups(const ActLds& l, const u32x4 (&xr)[XG][F32SRC ? 2 : 1], int nsrc, int K) {
   const int ngrp = K / 8, total = nsrc * ngrp;
@@ -176,9 +199,14 @@ __device__ __forceinline__ void stage_groups(const ActLds& l, const u32x4 (&xr)[
     if (base >= total) break;
     const int i = base + threadIdx.x;
     const bool ok = i < total;
-    float v[8];
-    group_values<F32SRC>(xr[it], ok, v);
-    stage_group(l, ok, ok ? i / ngrp : 0, ok ? i % ngrp : 0, v, F32SRC);
+    if constexpr (!F32SRC) {
+      const u32x4 w = ok ? xr[it][0] : u32x4{0u, 0u, 0u, 0u};
+      stage_group_bf16(l, ok, ok ? i / ngrp : 0, ok ? i % ngrp : 0, w);
+    } else {
+      float v[8];
+      group_values<F32SRC>(xr[it], ok, v);
+      stage_group(l, ok, ok ? i / ngrp : 0, ok ? i % ngrp : 0, v, F32SRC);
+    }
   }
 }
 

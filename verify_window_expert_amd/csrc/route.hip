@@ -361,33 +361,48 @@ __global__ __launch_bounds__(kFinalThreads) void k_route_final(RouteArgs a) {
 constexpr int kTierThreads = kMaxExpertsRoute;
 
 __global__ __launch_bounds__(kTierThreads) void k_tier(TierArgs a) {
-  __shared__ float s_c[kTierThreads];
-  __shared__ uint8_t s_res[kTierThreads];
+  // each expert's place as one unsigned 64-bit key: its list (outside the tier 0,
+  // resident 1; 2 = no expert), then the count's bits (counts are >= 0, so their bits
+  // order like the values; inverted for the outside list, largest first), then the
+  // expert index (ties: the lower index first). Its rank in its list is the number of
+  // smaller keys less the entries of the lists before it.
+  __shared__ __align__(16) uint64_t s_key[kTierThreads];
   __shared__ int s_in[kTierThreads], s_out[kTierThreads];
+  __shared__ float s_c[kTierThreads];
   __shared__ int s_n[2], s_fail;
   const int E = a.n_experts, e = threadIdx.x;
   float c = 0.f;
-  uint8_t res = 2;   // 2: no expert
+  uint32_t res = 2;
   if (e < E) {
-    c = fmaf(a.counts[e], a.decay, (float)__builtin_popcount((uint32_t)a.row_mask[e]));
+    const uint32_t m = a.row_mask[e];
+    const float c0 = a.counts[e];
+    if (a.resident) res = a.resident[e] ? 1u : 0u;   // loaded with the counts
+    c = fmaf(c0, a.decay, (float)__builtin_popcount(m));
     a.counts[e] = c;
-    if (a.resident) res = a.resident[e] ? 1 : 0;
   }
   if (!a.resident) return;
+  const uint32_t cb = __float_as_uint(c);
+  const uint64_t key = ((uint64_t)res << 40) | ((uint64_t)(res == 0 ? ~cb : cb) << 8) | (uint64_t)e;
+  s_key[e] = key;
   s_c[e] = c;
-  s_res[e] = res;
+  const uint64_t b0 = __ballot(res == 0), b1 = __ballot(res == 1);
   if (e < 2) s_n[e] = 0;
   if (e == 0) s_fail = kTierThreads;
   __syncthreads();
+  if ((e & 63) == 0) {
+    atomicAdd(&s_n[0], (int)__popcll(b0));
+    atomicAdd(&s_n[1], (int)__popcll(b1));
+  }
+  int below = 0;
+#pragma unroll 8
+  for (int j = 0; j < kTierThreads; j += 2) {
+    const uint64_t k0 = s_key[j], k1 = s_key[j + 1];
+    below += (k0 < key) + (k1 < key);
+  }
+  __syncthreads();
   if (res != 2) {
-    int rank = 0;
-    for (int j = 0; j < E; j++) {
-      const float cj = s_c[j];
-      if (s_res[j] != res) continue;
-      rank += res ? (cj < c || (cj == c && j < e)) : (cj > c || (cj == c && j < e));
-    }
+    const int rank = below - (res == 1 ? s_n[0] : 0);
     if (res) s_out[rank] = e; else s_in[rank] = e;
-    atomicAdd(&s_n[res], 1);
   }
   __syncthreads();
   const int limit = min(a.max_swaps, min(s_n[0], s_n[1]));
