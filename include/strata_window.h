@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define STRATA_WINDOW_ABI_VERSION 2
+#define STRATA_WINDOW_ABI_VERSION 3
 
 enum { STRATA_OK = 0, STRATA_EINVAL = -1, STRATA_EUNSUPPORTED = -2, STRATA_EHIP = -3 };
 enum { STRATA_F32 = 0, STRATA_BF16 = 1 };       /* activation dtypes                */

@@ -39,7 +39,11 @@ def test_library_exports_every_declared_symbol(sw):
 
 
 def test_abi_version(sw):
-    assert sw.library().strata_window_abi_version() == 2
+    """The built library reports the version its header declares."""
+    text = open(os.path.join(ROOT, "include", "strata_window.h")).read()
+    declared = int(re.search(r"#define STRATA_WINDOW_ABI_VERSION (\d+)", text).group(1))
+    assert declared == 3
+    assert sw.library().strata_window_abi_version() == declared
 
 
 def test_workspace_sizes(sw):

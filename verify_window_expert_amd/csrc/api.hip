@@ -42,7 +42,7 @@ struct MoeWs { size_t h, y, total; };
 MoeWs moe_ws(int rows, int hidden, int ffn, int top_k) {
   const size_t ent = (size_t)rows * top_k + rows;
   MoeWs w;
-  w.h = STRATA_WS_COUNTER_BYTES;
+  w.h = STRATA_WS_COUNTER_BYTES;                          // bf16 hi + lo per entry and input
   w.y = round_up(w.h + 4 * ent * ffn, 256);
   w.total = round_up(w.y + 4 * ent * hidden, 256);
   return w;
@@ -224,7 +224,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   g.n_active = route->n_active; g.active = route->active; g.offsets = route->offsets; g.entry_row = route->entry_row;
   g.row_mask = route->row_mask;
   g.max_slots = max_slots;
-  g.h = (float*)((char*)ws + w.h);
+  g.h_img = (uint32_t*)((char*)ws + w.h);
   const sw::Prof pg = prof(prof_events, 0), pd = prof(prof_events, 2);
   if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
 
@@ -235,7 +235,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   d.n_active = route->n_active; d.active = route->active; d.offsets = route->offsets;
   d.entry_row = route->entry_row; d.entry_w = route->entry_w; d.row_mask = route->row_mask;
   d.entry_pos = route->entry_pos; d.row_w = route->row_w;
-  d.h = g.h; d.y = (float*)((char*)ws + w.y); d.out = out; d.x_next = x_next_bf16;
+  d.h_img = g.h_img; d.y = (float*)((char*)ws + w.y); d.out = out; d.x_next = x_next_bf16;
   d.n_ranges = n_ranges; d.max_slots = max_slots; d.top_k = top_k;
   return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
 }

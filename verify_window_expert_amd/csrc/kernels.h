@@ -27,7 +27,7 @@ struct GateUpArgs {
   QDev gate, up;
   const int32_t* n_active; const int32_t* active; const int32_t* offsets;
   const int32_t* entry_row; const uint8_t* row_mask;
-  float* h;                 // [entries][ffn]
+  uint32_t* h_img;          // [entries][ffn]: h as bf16 hi | lo << 16, in the permuted order
   int max_slots;            // capacity of the active array (offsets: max_slots + 1)
   int split;                // set by the launcher: waves per item (1 or 2), fixed by the
                             // shapes alone so a row's sums never depend on the window
@@ -39,7 +39,7 @@ struct DownArgs {
   const int32_t* n_active; const int32_t* active; const int32_t* offsets;
   const int32_t* entry_row; const float* entry_w; const uint8_t* row_mask;
   const int32_t* entry_pos; const float* row_w;
-  const float* h;           // [entries][ffn]
+  const uint32_t* h_img;    // as GateUpArgs
   float* y;                 // [rows][top_k + 1][hidden]: row r's experts in ascending id order
   float* out; uint16_t* x_next;
   int n_ranges;             // 64-row output ranges

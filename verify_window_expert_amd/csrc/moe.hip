@@ -190,6 +190,38 @@ __device__ __forceinline__ void stage_group_bf16(const ActLds& l, bool ok, int j
   }
 }
 
+// A group of 8 inputs already split into bf16 hi | lo << 16 words in the image order
+// (the down kernel's h): byte permutes give the hi and lo words, and the block sums add
+// the group's values in image order, then over the 4 lanes of the block.
+__device__ __forceinline__ void stage_group_hl(const ActLds& l, bool ok, int j, int u, const u32x4 (&w)[2]) {
+  u32x4 ph, pl;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint32_t w0 = w[t >> 1][2 * (t & 1)], w1 = w[t >> 1][2 * (t & 1) + 1];
+    ph[t] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+    pl[t] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+  }
+  float shi = 0.f, slo = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const uint32_t word = w[e >> 2][e & 3];
+    shi += __uint_as_float(word << 16);
+    slo += __uint_as_float(word & 0xFFFF0000u);
+  }
+  shi += __shfl_xor(shi, 1);
+  shi += __shfl_xor(shi, 2);
+  slo += __shfl_xor(slo, 1);
+  slo += __shfl_xor(slo, 2);
+  if (ok) {
+    *(u32x4*)(l.xs + (size_t)j * l.stride + 8 * u) = ph;
+    *(u32x4*)(l.xs + (size_t)(8 + j) * l.stride + 8 * u) = pl;
+    if ((u & 3) == 0) {
+      l.sx[(u >> 2) * 16 + j] = shi;
+      l.sx[(u >> 2) * 16 + 8 + j] = slo;
+    }
+  }
+}
+
 template <int THREADS, int XG, bool F32SRC>
 __device__ __forceinline__ void stage_groups(const ActLds& l, const u32x4 (&xr)[XG][F32SRC ? 2 : 1], int nsrc, int K) {
   const int ngrp = K / 8, total = nsrc * ngrp;
@@ -209,6 +241,11 @@ __device__ __forceinline__ void stage_groups(const ActLds& l, const u32x4 (&xr)[
     }
   }
 }
+
+// Place of input k0 + k (k < 8) in its group of 8 in the image: the code conversion's
+// order holds input perm_q(e) at element e, so input k sits at element 2 (k % 4) + k / 4.
+// For the 16 inputs of a tile (k < 16): the group's base plus that place.
+__device__ __forceinline__ int tile_pos(int k) { return (k & 8) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
 // A lane's view of the image: its row (its column c, or the zero row) at its k-offset,
 // and its block-sum column.
@@ -461,7 +498,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   const CodeConsts cc = code_consts();
   f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
   int cu_j = 0, cu_g = 0;
-  // h = silu(gate) * up for the item's rows, from the finished sums (lanes < 32)
+  // h = silu(gate) * up for the item's rows, from the finished sums (lanes < 32 hold
+  // rows 0..7), split into its bf16 hi and lo parts (hi | lo << 16, one word) and stored
+  // at the input's place in its group of 8, the order the down kernel stages
+  const int f_pos = tile_pos(c);
   auto write_h = [&](const f32x4& gs, const f32x4& us) __attribute__((always_inline)) {
     const int item = me + cu_j * Wg;
     const int slot = item / tiles, tile = item % tiles, e = s_active[slot];
@@ -473,7 +513,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
       if (r < R && ((rmask >> r) & 1u)) {
         const int ent = ent0 + __builtin_popcount(rmask & ((1u << r) - 1u));
         const float gv = gs[i];
-        a.h[(long)ent * F + tile * 16 + c] = gv / (1.f + expf(-gv)) * us[i];
+        const float hv = gv / (1.f + expf(-gv)) * us[i];
+        const uint32_t hi = f32_to_bf16(hv);
+        const uint32_t lo = f32_to_bf16(hv - bf16_to_f32((uint16_t)hi));
+        a.h_img[(long)ent * F + tile * 16 + f_pos] = hi | (lo << 16);
       }
     }
   };
@@ -582,12 +625,21 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   const int my_tiles = t0 < tiles_h ? (tiles_h - t0 + stride - 1) / stride : 0;
   const int units = my_tiles * NG;
 
-  // the expert's h (XG groups of 8 per thread), and where each of its entries' y goes:
-  // row r's list of experts in ascending id order, position entry_pos
+  // the expert's h as the gate/up kernel wrote it (XG groups of 8 inputs per thread, two
+  // 16-byte words each: group i is row i / (F/8), inputs 8 (i % (F/8)) ..), and where
+  // each of its entries' y goes: row r's list of experts in ascending id order, position
+  // entry_pos
   const ActLds l = act_lds(smem, F, 16);
-  const float* hsrc = a.h + (long)e0 * F;
+  const int ngrp = F / 8, total = max(ne, 1) * ngrp;
+  const uint32_t* hsrc = a.h_img + (long)e0 * F;
   u32x4 hr[XG][2];
-  load_groups<kDnThreads, XG, true>(hr, hsrc, max(ne, 1), F);
+#pragma unroll
+  for (int it = 0; it < XG; it++) {
+    const int i = min(it * kDnThreads + tid, total - 1);
+    const u32x4* p = (const u32x4*)(hsrc + (long)(i / ngrp) * F + 8 * (i % ngrp));
+    hr[it][0] = p[0];
+    hr[it][1] = p[1];
+  }
   const int ej = e0 + min(lane, max(ne, 1) - 1);
   const int dst_row = a.entry_row[ej], dst_pos = a.entry_pos[ej];
   __builtin_amdgcn_sched_barrier(0);
@@ -598,7 +650,14 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   auto stage = [&]() __attribute__((always_inline)) {
     if (tid < kMaxRows) s_ydst[tid] = dst_row * (a.top_k + 1) + dst_pos;
     zero_absent<kDnThreads>(l, F, ne, true);
-    stage_groups<kDnThreads, XG, true>(l, hr, ne, F);   // the launcher picks XG to cover all groups
+    const int total_e = ne * ngrp;   // the launcher picks XG to cover them
+#pragma unroll
+    for (int it = 0; it < XG; it++) {
+      const int base = it * kDnThreads;
+      if (base >= total_e) break;
+      const int i = base + tid;
+      stage_group_hl(l, i < total_e, i < total_e ? i / ngrp : 0, i < total_e ? i % ngrp : 0, hr[it]);
+    }
   };
   if (units == 0) {
     stage();
@@ -797,7 +856,7 @@ static int launch_down_k(const DownArgs& a, size_t lds, int max_slots, hipStream
 
 template <int BITS>
 static int launch_down_bits(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
-  // h groups (8 floats) of up to 8 rows per thread, all loaded up front (8 * ffn / 8)
+  // h groups (8 inputs) of up to 8 rows per thread, all loaded up front (8 * ffn / 8)
   if (a.ffn <= 1 * kDnThreads) return launch_down_k<BITS, 1>(a, lds, max_slots, s, p);
   if (a.ffn <= 2 * kDnThreads) return launch_down_k<BITS, 2>(a, lds, max_slots, s, p);
   if (a.ffn <= 4 * kDnThreads) return launch_down_k<BITS, 4>(a, lds, max_slots, s, p);
