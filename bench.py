@@ -2,8 +2,10 @@
 """Throughput of the batched verify-window MoE layer on one MI355X.
 
 A step is one verify window through the whole layer: router GEMV + softmax + top-k +
-per-expert row grouping (strata_window_route), then fused dequant gate/up + SwiGLU, down
-and the weighted combine with the shared expert (strata_window_moe). The default
+per-expert row grouping, fused dequant gate/up + SwiGLU, down and the weighted combine with
+the shared expert. By default one strata_window_layer call per window (router GEMV, then
+gate/up whose workgroups take the routing themselves, then down and combine); --path split
+runs strata_window_route and then strata_window_moe instead. The default
 workload is the 8-row window (4 slots x token + MTP proposal, Zipf(1.1) router prior,
 correlated pairs) of a 2048-hidden / 768-ffn / 128-expert top-8 layer with 4-bit block
 quantization. --config 3 runs the 24-layer stack with the 8-bit head instead (a step is
@@ -48,6 +50,9 @@ def parse():
     p.add_argument("--inflight", type=int, default=1,
                    help="independent windows in flight (windows alternate over this many streams, "
                         "like pipelined slot groups); 1 = one window after the other")
+    p.add_argument("--path", choices=["layer", "split"], default="layer",
+                   help="layer: strata_window_layer (router, then gate/up with the routing in every "
+                        "workgroup, then down); split: strata_window_route, then strata_window_moe")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget (0: skip)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first copy this many MiB device to device three times (a dispatch of known "
@@ -104,8 +109,10 @@ def counter_traffic(kernel, workload):
 class Steps:
     """Device state of K steps: layers, windows, per-step routing outputs, workspaces."""
 
-    def __init__(self, cfg, n_layers, n_windows, steps, sw, torch, synth, DevLayer, to_dev_x, inflight=1):
+    def __init__(self, cfg, n_layers, n_windows, steps, sw, torch, synth, DevLayer, to_dev_x, inflight=1,
+                 path="layer"):
         self.cfg, self.sw, self.torch = cfg, sw, torch
+        self.path = path
         R, H, E, k = cfg.rows, cfg.hidden, cfg.experts, cfg.top_k
         t0 = time.time()
         self.layers = []
@@ -142,19 +149,26 @@ class Steps:
             self.routes.append(ro)
         # one set of workspaces and outputs per window in flight
         self.ws_r = [sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E)) for _ in range(inflight)]
-        self.ws_m = [sw.workspace(sw.workspace_bytes(1, R, H, cfg.ffn, E, k)) for _ in range(inflight)]
+        self.ws_m = [sw.workspace(sw.workspace_bytes(1 if path == "split" else 3, R, H, cfg.ffn, E, k))
+                     for _ in range(inflight)]
         self.out = [torch.empty(R, H, dtype=torch.float32, device=dev) for _ in range(inflight)]
         self.inflight = inflight
 
-    def step(self, i, prof_route=None, prof_moe=None):
+    def step(self, i, prof=None):
+        """One window; prof: None or 6 event handles (router start/end, gate/up start/end,
+        down start/end)."""
         cfg, sw = self.cfg, self.sw
         dl = self.layers[i % len(self.layers)]
         x = self.xs[i % len(self.xs)]
         j = i % self.inflight
+        if self.path == "layer":
+            sw.strata_window_layer(x, dl.gate_w, dl.bias, cfg.top_k, dl.gate, dl.up, dl.down, *dl.sh,
+                                   route=self.routes[i], out=self.out[j], ws=self.ws_m[j], prof=prof)
+            return
         ro = sw.strata_window_route(x, dl.gate_w, dl.bias, cfg.top_k, out=self.routes[i], ws=self.ws_r[j],
-                                    prof=prof_route)
+                                    prof=None if prof is None else prof[:2])
         sw.strata_window_moe(x, dl.gate, dl.up, dl.down, *dl.sh, ro, out=self.out[j], ws=self.ws_m[j],
-                             prof=prof_moe)
+                             prof=None if prof is None else prof[2:])
 
     def distinct_experts(self, steps):
         return (self.big["n_active"][:steps, 0] - 1).cpu().numpy()
@@ -198,14 +212,15 @@ def window_tail_kernels(torch, sw, st, cfg, P):
     R, E = cfg.rows, cfg.experts
     g = torch.Generator(device="cpu").manual_seed(7)
     argmax = torch.randint(0, 151936, (R,), generator=g, dtype=torch.int32).cuda()
+    mtp = R % 2 == 0                        # token/proposal pairs; one row per slot otherwise
     prop = argmax[0::2].clone()
     prop[1::2] += 1                         # half the proposals kept
     counts = torch.zeros(E, dtype=torch.float32, device="cuda")
     resident = (torch.arange(E) % 3 == 0).to(torch.uint8).cuda()
-    tok, ntok, nacc = sw.strata_window_accept(argmax, prop)
+    tok, ntok, nacc = sw.strata_window_accept(argmax, prop, mtp=mtp)
     out = {}
-    for name, fn in (("accept", lambda i, ev: sw.strata_window_accept(argmax, prop, tokens=tok, n_tokens=ntok,
-                                                                      n_accepted=nacc, prof=ev)),
+    for name, fn in (("accept", lambda i, ev: sw.strata_window_accept(argmax, prop, mtp=mtp, tokens=tok,
+                                                                      n_tokens=ntok, n_accepted=nacc, prof=ev)),
                      ("tier_count", lambda i, ev: sw.strata_window_tier(st.routes[i].row_mask, counts, 0.875,
                                                                         prof=ev)),
                      ("tier_select", lambda i, ev: sw.strata_window_tier(st.routes[i].row_mask, counts, 0.875,
@@ -264,7 +279,8 @@ def main():
     cfg = synth.config(args.config, **({"rows": args.rows} if args.rows else {}))
     K, W = args.steps, args.warmup
     NF = max(1, args.inflight)
-    st = Steps(cfg, args.layers, args.windows, max(K, args.prof_steps), sw, torch, synth, DevLayer, to_dev_x, NF)
+    st = Steps(cfg, args.layers, args.windows, max(K, args.prof_steps), sw, torch, synth, DevLayer, to_dev_x, NF,
+               args.path)
 
     for i in range(W):
         st.step(i)
@@ -275,8 +291,7 @@ def main():
     evs = events(torch, 6 * P)
     for i in range(P):
         e = evs[6 * i: 6 * i + 6]
-        st.step(i, prof_route=[e[0].cuda_event, e[1].cuda_event],
-                prof_moe=[e[2].cuda_event, e[3].cuda_event, e[4].cuda_event, e[5].cuda_event])
+        st.step(i, prof=[ev.cuda_event for ev in e])
     torch.cuda.synchronize()
     d_route = [evs[6 * i].elapsed_time(evs[6 * i + 1]) for i in range(P)]
     d_gu = [evs[6 * i + 2].elapsed_time(evs[6 * i + 3]) for i in range(P)]
@@ -328,8 +343,8 @@ def main():
     traffic = counter_traffic("k_gateup", f"config{cfg.cid}")
     roof = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "k_gateup (fused 4-bit dequant gate/up matvec + SwiGLU)" if cfg.bits == 4 else
-                      "k_gateup (fused 2-bit dequant gate/up matvec + SwiGLU)",
+            "kernel": ("k_gateup (fused {}-bit dequant gate/up matvec + SwiGLU{})".format(
+                cfg.bits, ", with the window's top-k and grouping in every workgroup" if args.path == "layer" else "")),
             "avg_launch_us": round(1e3 * sum(d_gu) / P, 3),
             "algorithmic_bytes_per_launch": round(sum(gu_bytes) / P)}
 
@@ -350,7 +365,7 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": workload, "config_id": cfg.cid, "rows": R, "hidden": H, "ffn": F, "experts": E,
                    "top_k": cfg.top_k, "bits": cfg.bits, "layer_instances": args.layers,
-                   "windows_in_flight": NF},
+                   "windows_in_flight": NF, "path": args.path},
         "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "mean_distinct_experts": round(float(U.mean()), 2),
         "unique_weight_bytes_per_window": round(bytes_total / K),

@@ -29,7 +29,9 @@
  *     hipEvent_t handles (created by the caller, timing enabled) that the dispatches
  *     themselves record at the start and end of each kernel, for measuring kernel
  *     durations: route {start of its first kernel, end of its last}; moe {gate/up
- *     start, gate/up end, down start, end of the combine}; head {start, end}. A NULL
+ *     start, gate/up end, down start, end of the combine}; layer {router GEMV start, end,
+ *     gate/up (with the routing) start, end, down start, end of the combine}; head
+ *     {start, end}; accept and tier {start, end}. A NULL
  *     entry is skipped. Pass NULL while the stream is being captured into a graph.
  *   - Workspace `ws`: at least strata_window_workspace(...) bytes of scratch (partial
  *     sums and intermediates; the first STRATA_WS_COUNTER_BYTES bytes are reserved).
@@ -178,6 +180,26 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
                       void* ws, size_t ws_bytes, void* const* prof_events);
 
 /*
+ * strata_window_layer - the whole MoE layer of one window in one call: what
+ * strata_window_route and then strata_window_moe compute, with the same arguments and
+ * outputs (route receives the window's routing, as strata_window_route writes it), in
+ * three kernels instead of five: the router's GEMV, then gate/up whose every workgroup
+ * takes top-k, softmax and grouping from the GEMV's partial sums itself, then down and
+ * the combine. (Strata docs/BATCHING.md, opening paragraph: the router, the shared expert
+ * and every routed expert the rows use are read once per window for all of them.)
+ *   ws: at least strata_window_workspace(3, ...) bytes.
+ * Errors: those of strata_window_route and strata_window_moe, and a workspace smaller
+ * than strata_window_workspace(3, ...).
+ */
+int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
+                        const float* gate_w, const float* logit_bias, int flags,
+                        const strata_qmat* gate, const strata_qmat* up, const strata_qmat* down,
+                        const strata_qmat* sh_gate, const strata_qmat* sh_up,
+                        const strata_qmat* sh_down, int n_experts, int top_k,
+                        const strata_route_out* route, const void* residual, float* out,
+                        uint16_t* x_next_bf16, void* ws, size_t ws_bytes, void* const* prof_events);
+
+/*
  * strata_window_head - the output head of the window (Strata docs/BATCHING.md, opening
  * paragraph: the head is read once per window; docs/MULTI_GPU.md "What each card
  * holds": the last card runs it): logits[r][v] = sum_h W[v][h] * x[r][h] over an 8-bit
@@ -235,7 +257,8 @@ int strata_window_tier(void* stream, const uint8_t* row_mask, int n_experts, flo
                        uint8_t* resident, int max_swaps, float min_gain, int32_t* swaps,
                        int32_t* n_swaps, void* const* prof_events);
 
-/* Workspace bytes for which = 0 (route), 1 (moe), 2 (head); 0 for invalid arguments. */
+/* Workspace bytes for which = 0 (route), 1 (moe), 2 (head), 3 (layer); 0 for invalid
+ * arguments. */
 size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts,
                                int top_k, int vocab);
 

@@ -34,12 +34,18 @@ def oracle_mats(layer, cfg):
             q(layer.sh_gate, 1, F, H), q(layer.sh_up, 1, F, H), q(layer.sh_down, 1, H, F))
 
 
-def gpu_window(dl, x_dev, top_k, renorm=False, residual=False, x_next=False):
-    """Route + experts of one window on the GPU. Returns (route host dict, out np, x_next np)."""
-    ro = sw.strata_window_route(x_dev, dl.gate_w, dl.bias, top_k, renorm=renorm)
+def gpu_window(dl, x_dev, top_k, renorm=False, residual=False, x_next=False, layer=False):
+    """Route + experts of one window on the GPU, by strata_window_route and then
+    strata_window_moe, or (layer) by strata_window_layer. Returns (route host dict, out np,
+    x_next np)."""
     xn = torch.empty(x_dev.shape, dtype=torch.bfloat16, device="cuda") if x_next else None
-    out = sw.strata_window_moe(x_dev, dl.gate, dl.up, dl.down, *dl.sh, ro,
-                               residual=x_dev if residual else None, x_next=xn)
+    if layer:
+        out, ro = sw.strata_window_layer(x_dev, dl.gate_w, dl.bias, top_k, dl.gate, dl.up, dl.down, *dl.sh,
+                                         renorm=renorm, residual=x_dev if residual else None, x_next=xn)
+    else:
+        ro = sw.strata_window_route(x_dev, dl.gate_w, dl.bias, top_k, renorm=renorm)
+        out = sw.strata_window_moe(x_dev, dl.gate, dl.up, dl.down, *dl.sh, ro,
+                                   residual=x_dev if residual else None, x_next=xn)
     torch.cuda.synchronize()
     xnn = None if xn is None else xn.view(torch.int16).cpu().numpy().view(np.uint16)
     return ro.host(), out.cpu().numpy(), xnn

@@ -197,3 +197,25 @@ def test_tier_rejects(sw):
     assert call(gain=float("inf")) == sw.STRATA_EINVAL
     assert call(swp=None) == sw.STRATA_EINVAL
     assert call(ns=None) == sw.STRATA_EINVAL
+
+
+def test_layer_rejects_and_workspace(sw):
+    L = sw.library()
+    assert L.strata_window_workspace(3, 8, 2048, 768, 128, 8, 0) >= \
+        L.strata_window_workspace(1, 8, 2048, 768, 128, 8, 0) + 8 * 8 * 128 * 4
+    assert L.strata_window_workspace(3, 8, 2048, 768, 0, 8, 0) == 0
+    ro = route_out(sw)
+    m = dict(gate=qm(sw, 768, 2048, 4, 128), up=qm(sw, 768, 2048, 4, 128), down=qm(sw, 2048, 768, 4, 128),
+             sh_gate=qm(sw, 768, 2048, 4, 1), sh_up=qm(sw, 768, 2048, 4, 1), sh_down=qm(sw, 2048, 768, 4, 1))
+
+    def call(rows=8, H=2048, F=768, E=128, k=8, flags=0, gw=A, ws_bytes=1 << 30, mats=m, out=A):
+        return L.strata_window_layer(None, A, 1, rows, H, F, gw, None, flags,
+                                     *[ctypes.byref(mats[n]) for n in ("gate", "up", "down", "sh_gate", "sh_up",
+                                                                      "sh_down")],
+                                     E, k, ctypes.byref(ro), None, out, None, A, ws_bytes, None)
+    assert call(rows=9) == sw.STRATA_EINVAL
+    assert call(gw=0) == sw.STRATA_EINVAL                # router weights
+    assert call(flags=2) == sw.STRATA_EINVAL             # route flags
+    assert call(out=A + 4) == sw.STRATA_EINVAL           # moe output
+    assert call(F=640) == sw.STRATA_EINVAL               # matrices of another shape
+    assert call(ws_bytes=L.strata_window_workspace(1, 8, 2048, 768, 128, 8, 0)) == sw.STRATA_EINVAL

@@ -1,0 +1,91 @@
+"""GPU parity of the fused layer entry point (strata_window_layer: the router's GEMV,
+then gate/up with the routing taken in every workgroup, then down and the combine)
+against the CPU oracle, through the C ABI; and its agreement with the two-call path."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import verify_window_expert_amd as sw  # noqa: E402
+from gpu_helpers import (REL_TOL, DevLayer, assert_route_equal, gpu_window, oracle_mats,  # noqa: E402
+                         oracle_window, row_rel_err, to_dev_x, topk_gap)
+
+_layers = {}
+
+
+def layer_for(cfg):
+    if cfg not in _layers:
+        if len(_layers) > 4:
+            _layers.clear()
+        L = synth.make_layer(cfg, 0)
+        _layers[cfg] = (L, DevLayer(L, cfg), oracle_mats(L, cfg))
+    return _layers[cfg]
+
+
+def check(cfg, window=0, renorm=False, residual=False, x_next=False):
+    L, dl, mats = layer_for(cfg)
+    x = synth.make_window(cfg, window)
+    print(f"[layer] cid={cfg.cid} H={cfg.hidden} E={cfg.experts} bits={cfg.bits} R={x.shape[0]} "
+          f"window={window} renorm={renorm} residual={residual}", flush=True)
+    gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next, layer=True)
+    orc, oout, oxn = oracle_window(L, mats, x, cfg, renorm, residual, x_next)
+    assert topk_gap(orc["logits"], cfg.top_k) > 1e-9, "near-tie in the routing of this seed"
+    assert_route_equal(gr, orc, cfg)
+    err = row_rel_err(gout, oout)
+    assert err <= REL_TOL, err
+    return dl, x, gr, gout, gxn, oxn
+
+
+@pytest.mark.parametrize("window", [0, 1])
+def test_layer_config0(window):
+    check(synth.config(0), window)
+
+
+def test_layer_config0_renorm_residual_x_next():
+    _, _, _, gout, gxn, oxn = check(synth.config(0), 2, renorm=True, residual=True, x_next=True)
+    # x_next is the bf16 rounding of the GPU's own output
+    want = (np.frombuffer(np.ascontiguousarray(gout, np.float32).tobytes(), np.uint32))
+    rne = ((want + 0x7FFF + ((want >> 16) & 1)) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(gxn.ravel(), rne)
+
+
+def test_layer_config1():
+    check(synth.config(1), 0)
+
+
+@pytest.mark.parametrize("window", [0, 1, 2])
+def test_layer_config2(window):
+    check(synth.config(2), window)
+
+
+@pytest.mark.parametrize("rows", synth.CONFIG4_ROWS)
+def test_layer_config4_rows(rows):
+    check(synth.config(4, rows=rows), 0)
+
+
+def test_layer_row_equals_row_alone_bitwise():
+    cfg = synth.config(2)
+    dl, x, _, gout, _, _ = check(cfg, 3)
+    for r in range(x.shape[0]):
+        print(f"[layer] row {r} alone", flush=True)
+        _, g1, _ = gpu_window(dl, to_dev_x(x[r:r + 1]), cfg.top_k, layer=True)
+        assert np.array_equal(g1[0].view(np.uint32), gout[r].view(np.uint32)), r
+
+
+def test_layer_matches_two_call_path():
+    cfg = synth.config(2)
+    L, dl, _ = layer_for(cfg)
+    xd = to_dev_x(synth.make_window(cfg, 5))
+    print("[layer] against route + moe", flush=True)
+    gr1, o1, _ = gpu_window(dl, xd, cfg.top_k, layer=True)
+    gr2, o2, _ = gpu_window(dl, xd, cfg.top_k, layer=False)
+    for k in ("topk_idx", "active", "offsets", "entry_row", "entry_pos", "row_mask"):
+        assert np.array_equal(gr1[k], gr2[k]), k
+    np.testing.assert_allclose(gr1["topk_w"], gr2["topk_w"], rtol=1e-6)
+    assert row_rel_err(o1, o2) <= 1e-5

@@ -56,6 +56,9 @@ def library():
         L.strata_window_moe.restype = I
         L.strata_window_head.argtypes = [P, P, I, I, I, ctypes.POINTER(CQMat), I, P, P, P, S, P]
         L.strata_window_head.restype = I
+        L.strata_window_layer.argtypes = [P, P, I, I, I, I, P, P, I] + [ctypes.POINTER(CQMat)] * 6 + \
+            [I, I, ctypes.POINTER(CRouteOut), P, P, P, P, S, P]
+        L.strata_window_layer.restype = I
         L.strata_window_accept.argtypes = [P, P, I, I, I, P, P, P, P, P]
         L.strata_window_accept.restype = I
         L.strata_window_tier.argtypes = [P, P, I, P, ctypes.c_float, P, I, ctypes.c_float, P, P, P]
@@ -225,6 +228,36 @@ def strata_window_moe(x, gate, up, down, sh_gate, sh_up, sh_down, route, residua
                                        route.top_k, _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws),
                                        ws.numel(), _events(prof)))
     return out
+
+
+def strata_window_layer(x, gate_w, bias, top_k, gate, up, down, sh_gate, sh_up, sh_down, renorm=False,
+                        route=None, residual=None, out=None, x_next=None, ws=None, stream=None, prof=None):
+    """The whole layer of one window in one call (router, then experts). Returns
+    (out [rows, hidden] float32, the window's RouteOut); x_next filled if given.
+    prof: None or [router start, end, gate/up start, end, down start, end] handles."""
+    _need(x, "x"); _need(gate_w, "gate_w")
+    if bias is not None:
+        _need(bias, "bias")
+    rows, hidden = x.shape
+    E = gate_w.shape[0]
+    ffn = gate.rows
+    route = RouteOut(rows, E, top_k, x.device) if route is None else route
+    if out is None:
+        out = torch.empty(rows, hidden, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(workspace_bytes(3, rows, hidden, ffn, E, top_k), x.device)
+    if residual is not None:
+        _need(residual, "residual")
+    if x_next is not None:
+        _need(x_next, "x_next")
+    qs = [q.c() for q in (gate, up, down, sh_gate, sh_up, sh_down)]
+    ro = route.c()
+    _check(library().strata_window_layer(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ffn, _ptr(gate_w),
+                                         _ptr(bias), STRATA_ROUTE_RENORM if renorm else 0,
+                                         *[ctypes.byref(q) for q in qs], E, top_k, ctypes.byref(ro),
+                                         _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws), ws.numel(),
+                                         _events(prof)))
+    return out, route
 
 
 def strata_window_head(x, head, logits=True, argmax=None, ws=None, stream=None, prof=None):

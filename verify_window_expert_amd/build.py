@@ -19,14 +19,35 @@ def sources():
 
 
 def build(verbose=False):
-    """Compile every HIP source of the library into libstrata_window.so (always rebuilds)."""
+    """Compile every HIP source of the library into libstrata_window.so (always rebuilds):
+    one hipcc per source, run side by side, then one link."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmpdir = tempfile.mkdtemp(prefix="strata_build_")
+    objs, cmds = [], []
+    for src in sources():
+        obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append([hipcc] + [f for f in HIPCC_FLAGS if f != "-shared"] + ["-c", src, "-o", obj])
+
+    def run(cmd):
+        return subprocess.run(cmd, capture_output=True, text=True)
+
+    with ThreadPoolExecutor(max_workers=min(len(cmds), max(1, min(8, os.cpu_count() or 1)))) as ex:
+        results = list(ex.map(run, cmds))
+    for cmd, res in zip(cmds, results):
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed: " + " ".join(cmd) + "\n" + res.stdout + res.stderr)
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + sources() + ["-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
+    res = run(link)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+        raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
     if verbose:
-        print(" ".join(cmd))
+        print("\n".join(" ".join(c) for c in cmds + [link]))
+    for o in objs:
+        os.remove(o)
+    os.rmdir(tmpdir)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH

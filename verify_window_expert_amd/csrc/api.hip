@@ -48,6 +48,15 @@ MoeWs moe_ws(int rows, int hidden, int ffn, int top_k) {
   return w;
 }
 
+struct LayerWs { MoeWs moe; size_t partials, total; };
+LayerWs layer_ws(int rows, int hidden, int ffn, int E, int top_k) {
+  LayerWs w;
+  w.moe = moe_ws(rows, hidden, ffn, top_k);
+  w.partials = w.moe.total;
+  w.total = round_up(w.partials + sizeof(double) * rows * E * ((hidden + 511) / 512), 256);
+  return w;
+}
+
 struct HeadWs { size_t val, idx, total; };
 HeadWs head_ws(int rows, int vocab) {
   const size_t n = (size_t)sw::head_workgroups(vocab) * rows;
@@ -151,14 +160,19 @@ size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_e
     case 0: return n_experts >= 1 ? route_ws(rows, hidden, n_experts).total : 0;
     case 1: return (ffn >= 1 && top_k >= 1) ? moe_ws(rows, hidden, ffn, top_k).total : 0;
     case 2: return vocab >= 1 ? head_ws(rows, vocab).total : 0;
+    case 3: return (ffn >= 1 && top_k >= 1 && n_experts >= 1) ? layer_ws(rows, hidden, ffn, n_experts, top_k).total : 0;
     default: return 0;
   }
 }
 
-int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int hidden, const float* gate_w,
-                        const float* logit_bias, int n_experts, int top_k, int flags, const strata_route_out* out,
-                        void* ws, size_t ws_bytes, void* const* prof_events) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Checks of a route call and its argument block (partials at ws + partials_at).
+int prepare_route(const void* x, int x_dtype, int rows, int hidden, const float* gate_w, const float* logit_bias,
+                  int n_experts, int top_k, int flags, const strata_route_out* out, void* ws,
+                  size_t partials_at, sw::RouteArgs& a) {
   int rc;
   if ((rc = check_common(x, x_dtype, rows, hidden, ws))) return rc;
   if ((rc = check_experts(n_experts, top_k))) return rc;
@@ -167,27 +181,22 @@ int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int 
   if (logit_bias && !aligned(logit_bias, 16)) return fail(STRATA_EINVAL, "logit_bias not 16-byte aligned");
   if (flags & ~STRATA_ROUTE_RENORM) return fail(STRATA_EINVAL, "unknown route flags 0x%x", flags);
   if ((rc = check_route_out(out))) return rc;
-  const RouteWs w = route_ws(rows, hidden, n_experts);
-  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "route workspace %zu < %zu bytes", ws_bytes, w.total);
-
-  sw::RouteArgs a;
   a.x = x; a.x_dtype = x_dtype; a.rows = rows; a.hidden = hidden;
   a.gate_w = gate_w; a.bias = logit_bias; a.n_experts = n_experts; a.top_k = top_k;
   a.renorm = (flags & STRATA_ROUTE_RENORM) != 0;
-  a.partials = (double*)((char*)ws + w.partials);
+  a.partials = (double*)((char*)ws + partials_at);
   a.topk_idx = out->topk_idx; a.topk_w = out->topk_w; a.n_active = out->n_active; a.active = out->active;
   a.offsets = out->offsets; a.entry_row = out->entry_row; a.entry_w = out->entry_w; a.row_mask = out->row_mask;
   a.entry_pos = out->entry_pos; a.row_w = out->row_w;
-  const sw::Prof pr = prof(prof_events, 0);
-  return launch_status(sw::launch_route(a, (hipStream_t)stream, prof_events ? &pr : nullptr), "route");
+  return STRATA_OK;
 }
 
-int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
-                      const strata_qmat* gate, const strata_qmat* up, const strata_qmat* down,
-                      const strata_qmat* sh_gate, const strata_qmat* sh_up, const strata_qmat* sh_down,
-                      const strata_route_out* route, int n_experts, int top_k, const void* residual, float* out,
-                      uint16_t* x_next_bf16, void* ws, size_t ws_bytes, void* const* prof_events) {
-  g_err[0] = 0;
+// Checks of a moe call and its two argument blocks (intermediates in ws per w).
+int prepare_moe(const void* x, int x_dtype, int rows, int hidden, int ffn, const strata_qmat* gate,
+                const strata_qmat* up, const strata_qmat* down, const strata_qmat* sh_gate, const strata_qmat* sh_up,
+                const strata_qmat* sh_down, const strata_route_out* route, int n_experts, int top_k,
+                const void* residual, float* out, uint16_t* x_next_bf16, void* ws, const MoeWs& w,
+                sw::GateUpArgs& g, sw::DownArgs& d, int& max_slots) {
   int rc;
   if ((rc = check_common(x, x_dtype, rows, hidden, ws))) return rc;
   if ((rc = check_experts(n_experts, top_k))) return rc;
@@ -210,14 +219,8 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   if (lds_gu + kStaticLds > kLdsLimit || lds_dn + kStaticLds > kLdsLimit)
     return fail(STRATA_EUNSUPPORTED, "hidden %d / ffn %d need more than %zu bytes of LDS", hidden, ffn, kLdsLimit);
   if (ffn > STRATA_MAX_FFN) return fail(STRATA_EUNSUPPORTED, "ffn %d > %d", ffn, STRATA_MAX_FFN);
-  const MoeWs w = moe_ws(rows, hidden, ffn, top_k);
-  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "moe workspace %zu < %zu bytes", ws_bytes, w.total);
-  const int n_ranges = sw::down_ranges(hidden);
+  max_slots = std::min(n_experts, rows * top_k) + 1;
 
-  const int max_slots = std::min(n_experts, rows * top_k) + 1;
-  hipStream_t s = (hipStream_t)stream;
-
-  sw::GateUpArgs g;
   g.x = x; g.x_dtype = x_dtype; g.rows = rows; g.hidden = hidden; g.ffn = ffn; g.bits = bits;
   g.n_experts = n_experts;
   g.gate = qdev(gate, sh_gate); g.up = qdev(up, sh_up);
@@ -225,10 +228,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   g.row_mask = route->row_mask;
   g.max_slots = max_slots;
   g.h_img = (uint32_t*)((char*)ws + w.h);
-  const sw::Prof pg = prof(prof_events, 0), pd = prof(prof_events, 2);
-  if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
 
-  sw::DownArgs d;
   d.x_res = residual; d.x_dtype = x_dtype; d.rows = rows; d.hidden = hidden; d.ffn = ffn; d.bits = bits;
   d.n_experts = n_experts;
   d.down = qdev(down, sh_down);
@@ -236,7 +236,78 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   d.entry_row = route->entry_row; d.entry_w = route->entry_w; d.row_mask = route->row_mask;
   d.entry_pos = route->entry_pos; d.row_w = route->row_w;
   d.h_img = g.h_img; d.y = (float*)((char*)ws + w.y); d.out = out; d.x_next = x_next_bf16;
-  d.n_ranges = n_ranges; d.max_slots = max_slots; d.top_k = top_k;
+  d.max_slots = max_slots; d.top_k = top_k;
+  return STRATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int hidden, const float* gate_w,
+                        const float* logit_bias, int n_experts, int top_k, int flags, const strata_route_out* out,
+                        void* ws, size_t ws_bytes, void* const* prof_events) {
+  g_err[0] = 0;
+  sw::RouteArgs a;
+  const RouteWs w = route_ws(rows, hidden, n_experts);
+  if (int rc = prepare_route(x, x_dtype, rows, hidden, gate_w, logit_bias, n_experts, top_k, flags, out, ws,
+                             w.partials, a))
+    return rc;
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "route workspace %zu < %zu bytes", ws_bytes, w.total);
+  const sw::Prof pr = prof(prof_events, 0);
+  return launch_status(sw::launch_route(a, (hipStream_t)stream, prof_events ? &pr : nullptr), "route");
+}
+
+int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
+                      const strata_qmat* gate, const strata_qmat* up, const strata_qmat* down,
+                      const strata_qmat* sh_gate, const strata_qmat* sh_up, const strata_qmat* sh_down,
+                      const strata_route_out* route, int n_experts, int top_k, const void* residual, float* out,
+                      uint16_t* x_next_bf16, void* ws, size_t ws_bytes, void* const* prof_events) {
+  g_err[0] = 0;
+  sw::GateUpArgs g;
+  sw::DownArgs d;
+  int max_slots = 0;
+  const MoeWs w = moe_ws(rows, hidden, ffn, top_k);
+  if (int rc = prepare_moe(x, x_dtype, rows, hidden, ffn, gate, up, down, sh_gate, sh_up, sh_down, route, n_experts,
+                           top_k, residual, out, x_next_bf16, ws, w, g, d, max_slots))
+    return rc;
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "moe workspace %zu < %zu bytes", ws_bytes, w.total);
+  hipStream_t s = (hipStream_t)stream;
+  const sw::Prof pg = prof(prof_events, 0), pd = prof(prof_events, 2);
+  int rc;
+  if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
+  return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
+}
+
+int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
+                        const float* gate_w, const float* logit_bias, int flags, const strata_qmat* gate,
+                        const strata_qmat* up, const strata_qmat* down, const strata_qmat* sh_gate,
+                        const strata_qmat* sh_up, const strata_qmat* sh_down, int n_experts, int top_k,
+                        const strata_route_out* route, const void* residual, float* out, uint16_t* x_next_bf16,
+                        void* ws, size_t ws_bytes, void* const* prof_events) {
+  g_err[0] = 0;
+  sw::RouteArgs r;
+  sw::GateUpArgs g;
+  sw::DownArgs d;
+  int max_slots = 0;
+  const LayerWs w = layer_ws(rows, hidden, ffn > 0 ? ffn : 1, n_experts > 0 ? n_experts : 1, top_k > 0 ? top_k : 1);
+  int rc;
+  if ((rc = prepare_route(x, x_dtype, rows, hidden, gate_w, logit_bias, n_experts, top_k, flags, route, ws,
+                          w.partials, r)))
+    return rc;
+  if ((rc = prepare_moe(x, x_dtype, rows, hidden, ffn, gate, up, down, sh_gate, sh_up, sh_down, route, n_experts,
+                        top_k, residual, out, x_next_bf16, ws, w.moe, g, d, max_slots)))
+    return rc;
+  if (sw::gateup_lds_bytes(hidden, x_dtype) + kStaticLds + sw::route_core_lds_bytes() > kLdsLimit)
+    return fail(STRATA_EUNSUPPORTED, "hidden %d: the activations and the routing tables need more than %zu bytes "
+                "of LDS (use strata_window_route and strata_window_moe)", hidden, kLdsLimit);
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "layer workspace %zu < %zu bytes", ws_bytes, w.total);
+  g.route = r;
+  hipStream_t s = (hipStream_t)stream;
+  const sw::Prof pr = prof(prof_events, 0), pg = prof(prof_events, 2), pd = prof(prof_events, 4);
+  if ((rc = launch_status(sw::launch_route_logits(r, s, prof_events ? &pr : nullptr), "router"))) return rc;
+  if ((rc = launch_status(sw::launch_gateup_routed(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up")))
+    return rc;
   return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
 }
 

@@ -23,6 +23,7 @@ struct QDev {
 };
 
 struct GateUpArgs {
+  RouteArgs route;          // the fused layer: the routing core runs in every workgroup
   const void* x; int x_dtype; int rows, hidden, ffn, bits, n_experts;
   QDev gate, up;
   const int32_t* n_active; const int32_t* active; const int32_t* offsets;
@@ -86,6 +87,11 @@ inline void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, c
 // Launchers return the hipError_t of the launch (0 on success).
 int launch_route(const RouteArgs& a, hipStream_t s, const Prof* p);
 int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
+// the fused layer's gate/up: routing from a.route's partials in every workgroup (workgroup
+// 0 writes the routing outputs), then gate/up as launch_gateup
+int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
+// the router's GEMV alone (the fused layer's first kernel)
+int launch_route_logits(const RouteArgs& a, hipStream_t s, const Prof* p);
 int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
@@ -94,6 +100,7 @@ int head_workgroups(int vocab);
 int down_ranges(int hidden);
 // dynamic LDS of the gate/up and down kernels (the activation image)
 size_t gateup_lds_bytes(int hidden, int x_dtype);
+size_t route_core_lds_bytes();   // the fused layer's gate/up: the routing core's static LDS
 size_t down_lds_bytes(int ffn);
 
 }  // namespace sw

@@ -21,8 +21,7 @@
 // in flight: every wave issues all of its weight loads before it waits on any, the
 // activations are staged with 16-byte loads issued together, and routing metadata is
 // read once, in parallel, into LDS.
-#include "common.h"
-#include "kernels.h"
+#include "route_core.h"
 
 #include <type_traits>
 
@@ -392,18 +391,40 @@ constexpr int kGuWaves = 8, kGuThreads = 64 * kGuWaves;
 constexpr size_t kPartBytes = (size_t)kGuWaves * 2 * 32 * 8 * 4;   // [wave][parity][lane < 32][8]
 
 size_t gateup_split_lds_bytes(int hidden, int x_dtype) { return gateup_lds_bytes(hidden, x_dtype) + kPartBytes; }
+size_t route_core_lds_bytes() { return sizeof(RouteLds); }
 
 // s_waitcnt lgkmcnt(0) that the compiler does not move memory operations across
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int BITS, bool F32IN, int XG>
+// The routing core's LDS, present only in the fused layer's gate/up kernel.
+template <bool ROUTED>
+struct RouteLdsIf {
+  RouteLds v;
+};
+template <>
+struct RouteLdsIf<false> {};
+
+// ROUTED: the fused layer. Every workgroup runs the routing core (route_core.h) on the
+// router's partials and takes the window's tables from its own LDS (workgroup 0 also
+// writes the routing outputs); otherwise the tables come from strata_route_out.
+template <int BITS, bool F32IN, int XG, bool ROUTED>
 __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   constexpr int DEPTH = kGuDepth;
+  static_assert(kGuThreads == kRouteCoreThreads, "the routing core takes one wave per row");
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_active[kMaxSlots];
-  __shared__ int s_off[kMaxSlots + 1];
-  __shared__ uint8_t s_mask[kMaxExperts + 4];
+  __shared__ int s_act_g[kMaxSlots];
+  __shared__ int s_off_g[kMaxSlots + 1];
+  __shared__ uint8_t s_mask_g[kMaxExperts + 4];
+  __shared__ RouteLdsIf<ROUTED> rl;
   __shared__ int s_cnt[kGuWaves][2], s_done[kGuWaves][2];   // per group and item parity
+  int* s_active;
+  int* s_off;
+  uint8_t* s_mask;
+  if constexpr (ROUTED) {
+    s_active = rl.v.active; s_off = rl.v.off; s_mask = rl.v.rmask;
+  } else {
+    s_active = s_act_g; s_off = s_off_g; s_mask = s_mask_g;
+  }
   const int H = a.hidden, F = a.ffn, R = a.rows, E = a.n_experts;
   const int tiles = F / 16;
   // the wave index via readfirstlane: the compiler then knows it (and every count
@@ -417,17 +438,39 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   const ActLds l = act_lds(smem, H, F32IN ? 16 : 8);
   float* const s_part = (float*)(smem + act_lds_bytes(H, F32IN ? 16 : 8));   // k-split partials
   u32x4 xr[XG][F32IN ? 2 : 1];
-  load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
-  const int sa = a.active[min(tid, a.max_slots - 1)];
-  const int so = a.offsets[min(tid, a.max_slots)];
-  const uint8_t sm = a.row_mask[min(tid, E)];
-  // every wave's own copy of the active list (lane i: slots i and 64 + i), for the
-  // experts of its first units before the LDS tables exist
-  const int act0 = a.active[min(lane, a.max_slots - 1)], act1 = a.active[min(64 + lane, a.max_slots - 1)];
-  __builtin_amdgcn_sched_barrier(0);
-
-  // the active count: a wave-uniform scalar load in the same round
-  const int n_active = __builtin_amdgcn_readfirstlane(*a.n_active);
+  int sa = 0, so = 0, act0 = 0, act1 = 0, n_active = 0;
+  uint8_t sm = 0;
+  if constexpr (ROUTED) {
+    // the router's partials (requested first) and the activations; then the routing
+    // core, which leaves the window's tables in LDS (two candidate experts per lane up
+    // to 128 experts, else four: a branch on the expert count, the same in every wave)
+    if (E <= 2 * kWave) {
+      RouteRegs<2> rg;
+      route_load<2>(a.route, rg);
+      load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
+      __builtin_amdgcn_sched_barrier(0);
+      route_select<2>(a.route, rg, rl.v, blockIdx.x == 0);
+    } else {
+      RouteRegs<4> rg;
+      route_load<4>(a.route, rg);
+      load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
+      __builtin_amdgcn_sched_barrier(0);
+      route_select<4>(a.route, rg, rl.v, blockIdx.x == 0);
+    }
+    n_active = __builtin_amdgcn_readfirstlane(rl.v.n_active);
+  } else {
+    load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
+    sa = a.active[min(tid, a.max_slots - 1)];
+    so = a.offsets[min(tid, a.max_slots)];
+    sm = a.row_mask[min(tid, E)];
+    // every wave's own copy of the active list (lane i: slots i and 64 + i), for the
+    // experts of its first units before the LDS tables exist
+    act0 = a.active[min(lane, a.max_slots - 1)];
+    act1 = a.active[min(64 + lane, a.max_slots - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    // the active count: a wave-uniform scalar load in the same round
+    n_active = __builtin_amdgcn_readfirstlane(*a.n_active);
+  }
   const int S = a.split;
   const int gw = kGuWaves / S;                     // groups per workgroup
   const int part = wave / gw, gl = wave % gw;      // part of the k-range; group in the workgroup
@@ -467,9 +510,11 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   // without items takes a path of its own, so that in the working one the compiler sees
   // exactly the weight loads issued after the round and waits for the round only.
   auto stage = [&]() __attribute__((always_inline)) {
-    if (tid < a.max_slots) s_active[tid] = sa;
-    if (tid <= a.max_slots) s_off[tid] = so;
-    if (tid <= E) s_mask[tid] = sm;
+    if constexpr (!ROUTED) {
+      if (tid < a.max_slots) s_active[tid] = sa;
+      if (tid <= a.max_slots) s_off[tid] = so;
+      if (tid <= E) s_mask[tid] = sm;
+    }
     if (tid < kGuWaves * 2) { (&s_cnt[0][0])[tid] = 0; (&s_done[0][0])[tid] = 0; }
     zero_absent<kGuThreads>(l, H, R, F32IN);
     stage_groups<kGuThreads, XG, F32IN>(l, xr, R, H);   // the launcher picks XG to cover all groups
@@ -481,7 +526,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   }
   auto reg_of = [&](int j) __attribute__((always_inline)) {
     const int slot = min((me + j * Wg) / tiles, a.max_slots - 1);
-    return slot < 64 ? __builtin_amdgcn_readlane(act0, slot) : __builtin_amdgcn_readlane(act1, slot - 64);
+    if constexpr (ROUTED)   // the tables are already in LDS
+      return __builtin_amdgcn_readfirstlane(s_active[slot]);
+    else
+      return slot < 64 ? __builtin_amdgcn_readlane(act0, slot) : __builtin_amdgcn_readlane(act1, slot - 64);
   };
   set_item(reg_of(0), 0);
   static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { issue_next(d, reg_of); });
@@ -806,40 +854,51 @@ static int set_lds(size_t bytes) {
   return 0;
 }
 
-template <int BITS, bool F32IN, int XG>
+template <int BITS, bool F32IN, int XG, bool ROUTED>
 static int launch_gateup_k(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
-  if (int e = set_lds<k_gateup<BITS, F32IN, XG>>(lds)) return e;
-  launch(k_gateup<BITS, F32IN, XG>, dim3(persistent_grid<k_gateup<BITS, F32IN, XG>>(kGuThreads, lds, items, 1)),
+  auto kern = k_gateup<BITS, F32IN, XG, ROUTED>;
+  if (int e = set_lds<k_gateup<BITS, F32IN, XG, ROUTED>>(lds)) return e;
+  launch(kern, dim3(persistent_grid<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds, items, 1)),
          dim3(kGuThreads), lds, s, p, a);
   return 0;
 }
 
-template <int BITS, bool F32IN>
+template <int BITS, bool F32IN, bool ROUTED>
 static int launch_gateup_x(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
   // activation groups of 8 per thread, all loaded up front (rows * hidden / 8 <= 16 * 512
   // for every hidden whose image fits in LDS)
   const int groups = a.rows * (a.hidden / 8);
-  if (groups <= 4 * kGuThreads) return launch_gateup_k<BITS, F32IN, 4>(a, lds, items, s, p);
-  if (groups <= 8 * kGuThreads) return launch_gateup_k<BITS, F32IN, 8>(a, lds, items, s, p);
-  if (groups <= 16 * kGuThreads) return launch_gateup_k<BITS, F32IN, 16>(a, lds, items, s, p);
+  if (groups <= 4 * kGuThreads) return launch_gateup_k<BITS, F32IN, 4, ROUTED>(a, lds, items, s, p);
+  if (groups <= 8 * kGuThreads) return launch_gateup_k<BITS, F32IN, 8, ROUTED>(a, lds, items, s, p);
+  if (groups <= 16 * kGuThreads) return launch_gateup_k<BITS, F32IN, 16, ROUTED>(a, lds, items, s, p);
   return (int)hipErrorInvalidValue;
 }
 
-int launch_gateup(const GateUpArgs& a0, int max_slots, hipStream_t s, const Prof* p) {
+template <bool ROUTED>
+static int launch_gateup_any(const GateUpArgs& a0, int max_slots, hipStream_t s, const Prof* p) {
   GateUpArgs a = a0;
   const bool f32 = a.x_dtype == 0;
   // two waves per item when the k-groups split evenly and the partial-sum buffers fit
   // next to the activation image
   const int NG = a.hidden / (512 / a.bits);
-  a.split = (NG % 2 == 0 && gateup_split_lds_bytes(a.hidden, a.x_dtype) + 2048 <= 160 * 1024) ? 2 : 1;
+  const size_t static_lds = 2048 + (ROUTED ? sizeof(RouteLds) : 0);
+  a.split = (NG % 2 == 0 && gateup_split_lds_bytes(a.hidden, a.x_dtype) + static_lds <= 160 * 1024) ? 2 : 1;
   const size_t lds = a.split == 2 ? gateup_split_lds_bytes(a.hidden, a.x_dtype) : gateup_lds_bytes(a.hidden, a.x_dtype);
   const int items = max_slots * (a.ffn / 16);
   int e;
   if (a.bits == 4)
-    e = f32 ? launch_gateup_x<4, true>(a, lds, items, s, p) : launch_gateup_x<4, false>(a, lds, items, s, p);
+    e = f32 ? launch_gateup_x<4, true, ROUTED>(a, lds, items, s, p) : launch_gateup_x<4, false, ROUTED>(a, lds, items, s, p);
   else
-    e = f32 ? launch_gateup_x<2, true>(a, lds, items, s, p) : launch_gateup_x<2, false>(a, lds, items, s, p);
+    e = f32 ? launch_gateup_x<2, true, ROUTED>(a, lds, items, s, p) : launch_gateup_x<2, false, ROUTED>(a, lds, items, s, p);
   return e ? e : (int)hipGetLastError();
+}
+
+int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p) {
+  return launch_gateup_any<false>(a, max_slots, s, p);
+}
+
+int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p) {
+  return launch_gateup_any<true>(a, max_slots, s, p);
 }
 
 int down_ranges(int hidden) { return (hidden + kDownRange - 1) / kDownRange; }
