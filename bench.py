@@ -392,7 +392,7 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
     xs = [to_dev_x(synth.make_window(cfg, w)) for w in range(16)]
     routes = [sw.RouteOut(R, E, k) for _ in range(cfg.layers)]
     ws_r = sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E))
-    ws_m = sw.workspace(sw.workspace_bytes(1, R, H, F, E, k))
+    ws_m = sw.workspace(sw.workspace_bytes(1 if args.path == "split" else 3, R, H, F, E, k))
     ws_h = sw.workspace(sw.workspace_bytes(2, R, H, vocab=cfg.vocab))
     xa = torch.empty(R, H, dtype=torch.bfloat16, device="cuda")
     xb = torch.empty_like(xa)
@@ -401,21 +401,32 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
     am = torch.empty(8, dtype=torch.int32, device="cuda")
     n_act = torch.zeros(K, cfg.layers, dtype=torch.int32, device="cuda")
 
-    def step(i, record=True):
+    def step(i, record=True, prof_head=None):
         xa.copy_(xs[i % len(xs)])
         cur, nxt = xa, xb
         for l, dl in enumerate(layers):
-            ro = sw.strata_window_route(cur, dl.gate_w, dl.bias, k, out=routes[l], ws=ws_r)
-            sw.strata_window_moe(cur, dl.gate, dl.up, dl.down, *dl.sh, ro, residual=cur, out=out, x_next=nxt,
-                                 ws=ws_m)
+            if args.path == "layer":
+                _, ro = sw.strata_window_layer(cur, dl.gate_w, dl.bias, k, dl.gate, dl.up, dl.down, *dl.sh,
+                                               route=routes[l], residual=cur, out=out, x_next=nxt, ws=ws_m)
+            else:
+                ro = sw.strata_window_route(cur, dl.gate_w, dl.bias, k, out=routes[l], ws=ws_r)
+                sw.strata_window_moe(cur, dl.gate, dl.up, dl.down, *dl.sh, ro, residual=cur, out=out, x_next=nxt,
+                                     ws=ws_m)
             if record:
                 n_act[i, l].copy_(ro.n_active[0])
             cur, nxt = nxt, cur
-        sw.strata_window_head(cur, head, logits=logits, argmax=am, ws=ws_h)
+        sw.strata_window_head(cur, head, logits=logits, argmax=am, ws=ws_h, prof=prof_head)
 
     for i in range(W):
         step(i, record=False)
     torch.cuda.synchronize()
+    # the head's duration: events recorded by its own dispatches, over eager steps
+    P = 16
+    hev = events(torch, 2 * P)
+    for i in range(P):
+        step(i, record=False, prof_head=[hev[2 * i].cuda_event, hev[2 * i + 1].cuda_event])
+    torch.cuda.synchronize()
+    head_us = 1e3 * sum(hev[2 * i].elapsed_time(hev[2 * i + 1]) for i in range(P)) / P
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -442,9 +453,14 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "24 MoE layers (hidden 2048, ffn 768, 128 experts top-8 + shared, 4-bit) with "
                                    "residual, then an 8-bit head of vocab 151936 with argmax, 8-row window",
-                       "config_id": 3},
+                       "config_id": 3, "path": args.path},
             "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "roofline": None, "cpu_baseline": None}
+            "kernel_us": {"head": round(head_us, 3)},
+            "roofline": {"bound": "hbm", "achieved": round(b_h / (head_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(b_h / (head_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": None, "kernel": "k_head + k_head_argmax (8-bit head GEMV, vocab 151936)",
+                         "avg_launch_us": round(head_us, 3), "algorithmic_bytes_per_launch": round(b_h)},
+            "cpu_baseline": None}
     print(json.dumps(line), flush=True)
 
 

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sw {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -197,6 +199,35 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
 // 16x16x4 fp32: A lane l = A[l%16][l/16], B lane l = B[l/16][l%16], same C layout.
 __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ weight rings
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), unrolled: ring
+// slots are then compile-time register arrays.
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Units of a wave's work in rounds of DEPTH through the ring (unit u in slot u % DEPTH):
+// full rounds whose refills are all in range, one round whose refills stop at the end,
+// then the remainder. A round has no early exit: an exit inside the round would make the
+// compiler wait for every outstanding load at the loop head.
+template <int DEPTH, class Step>
+__device__ __forceinline__ void run_ring(int units, Step&& step) {
+  int u0 = 0;
+  for (; u0 + 2 * DEPTH <= units; u0 += DEPTH)
+    static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { step(d, true); });
+  if (u0 + DEPTH <= units) {
+    static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { step(d, u0 + d + DEPTH < units); });
+    u0 += DEPTH;
+  }
+  static_for<DEPTH>([&](auto d) __attribute__((always_inline)) {
+    if (u0 + d < units) step(d, false);
+  });
 }
 
 }  // namespace sw

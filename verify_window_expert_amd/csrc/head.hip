@@ -11,65 +11,153 @@
 // keep a binary16 remainder column); per block
 //     sum_k w x = scale * (D - 1152 * Sx),  D = sum (1152 + q) x.
 // A second one-workgroup launch reduces the per-workgroup argmax candidates.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace sw {
 
-constexpr int kHeadThreads = 256;
-constexpr int kHeadTilesPerWave = 4;
-constexpr int kHeadRange = 16 * 4 * kHeadTilesPerWave;    // vocab rows per workgroup
+constexpr int kHeadWaves = 8, kHeadThreads = 64 * kHeadWaves;
+#ifndef SW_HEAD_GRID
+#define SW_HEAD_GRID 256
+#endif
+#ifndef SW_HEAD_DEPTH
+#define SW_HEAD_DEPTH 8
+#endif
+constexpr int kHeadGrid = SW_HEAD_GRID;     // workgroups (one per compute unit of the MI355X)
+constexpr int kHeadDepth = SW_HEAD_DEPTH;   // units (one 16-row x 64-input chunk) in flight per wave
 
-int head_workgroups(int vocab) { return (vocab + kHeadRange - 1) / kHeadRange; }
+int head_workgroups(int vocab) {
+  const int tiles = (vocab + 15) / 16;
+  return std::min(kHeadGrid, (tiles + kHeadWaves - 1) / kHeadWaves);
+}
 
 static size_t head_lds_bytes(int H, int rows) {
   return (size_t)rows * (H + 8) * 2 + (size_t)(H / 32) * 16 * 4;
 }
 
-template <bool F32IN>
+// Wave w of workgroup b owns vocabulary tiles (16 rows) t = w * grid + b, + waves ...; it
+// streams their (tile, 64-input k-group) chunks through a ring of kHeadDepth units, the
+// first ring requested before the activations are staged. Per unit and 32-input block:
+// one f16 MFMA D = sum (1152 + q) x times the block's scale; the -1152 * scale * Sx
+// terms of the unit's two blocks by one fp32 MFMA on a second accumulator. After a
+// tile: logits (optional) and the lanes' running argmax; at the end, the workgroup's
+// candidates per row go to the workspace for k_head_argmax.
+template <bool F32IN, int XG>
 __global__ __launch_bounds__(kHeadThreads) void k_head(HeadArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float s_scale[kMaxRows], s_unscale[kMaxRows];
-  __shared__ float s_bv[4][kMaxRows];
-  __shared__ int s_bi[4][kMaxRows];
+  __shared__ uint32_t s_maxbits[kMaxRows];
+  __shared__ float s_bv[kHeadWaves][kMaxRows];
+  __shared__ int s_bi[kHeadWaves][kMaxRows];
+  constexpr int D = kHeadDepth;
   const int H = a.hidden, R = a.rows, V = a.vocab;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool f32in = a.x_dtype == 0;
-  const int nrows = f32in ? 16 : 8;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int c = lane & 15, q = lane >> 4;
+  const int nrows = F32IN ? 16 : 8;
   const int stride = H + 8;
   _Float16* xs = (_Float16*)smem;
   float* sx = (float*)(smem + (size_t)nrows * stride * 2);
+  const int NG = H / 64;                       // k-groups of 64 inputs = 2 blocks
+  const int tiles = V / 16;
+  const int TW = gridDim.x * kHeadWaves;
+  const int gw = wave * gridDim.x + blockIdx.x;   // wave-major (measured faster than block-major)
+  const int my_tiles = gw < tiles ? (tiles - gw + TW - 1) / TW : 0;
+  const int units = my_tiles * NG;
 
-  // per-row power-of-two scale: largest magnitude into [2^14, 2^15)
-  for (int r = wave; r < R; r += 4) {
-    float m = 0.f;
-    for (int h = lane; h < H; h += kWave) m = fmaxf(m, fabsf(load_x<F32IN>(a.x, (long)r * H + h)));
+  // the activations: XG groups of 8 per thread (group i: row i / (H/8)), all at once
+  const int ngrp = H / 8, total = R * ngrp;
+  u32x4 xr[XG][F32IN ? 2 : 1];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) {
-      int ex = 0;
-      if (m > 0.f) frexpf(m, &ex);        // m = f * 2^ex, f in [0.5, 1)
-      const int sh = m > 0.f ? 15 - ex : 0;
-      s_scale[r] = ldexpf(1.f, sh);
-      s_unscale[r] = ldexpf(1.f, -sh);
+  for (int it = 0; it < XG; it++) {
+    const int i = min(it * kHeadThreads + tid, total - 1);
+    if constexpr (F32IN) {
+      const u32x4* p = (const u32x4*)((const float*)a.x + (long)(i / ngrp) * H + 8 * (i % ngrp));
+      xr[it][0] = p[0];
+      xr[it][F32IN ? 1 : 0] = p[1];
+    } else {
+      xr[it][0] = *(const u32x4*)((const uint16_t*)a.x + (long)(i / ngrp) * H + 8 * (i % ngrp));
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the first ring of weights (past the last unit the ring stays on the last tile)
+  const u32x4* codes = (const u32x4*)a.codes;
+  const uint32_t* meta = (const uint32_t*)a.meta;
+  u32x4 rc[D];
+  uint32_t rm[D];
+  int is_j = 0, is_g = 0;
+  auto issue = [&](auto d_) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_)::value;
+    const long chunk = (long)(gw + is_j * TW) * NG + is_g;
+    // read once per window: non-temporal loads (measured faster than plain ones here)
+    rc[d] = __builtin_nontemporal_load(codes + chunk * 64 + lane);
+    rm[d] = __builtin_nontemporal_load(meta + chunk * 16 + c);
+    if (++is_g == NG) {
+      is_g = 0;
+      if (is_j + 1 < my_tiles) ++is_j;
+    }
+  };
+  if (units > 0) static_for<D>([&](auto d) __attribute__((always_inline)) { issue(d); });
+  __builtin_amdgcn_sched_barrier(0);
+
+  // per-row power-of-two scale (largest magnitude into [2^14, 2^15)), from the loaded
+  // groups: each thread's maximum, combined in LDS (magnitudes order as their bits)
+  if (tid < kMaxRows) s_maxbits[tid] = 0u;
   for (int i = tid; i < (H / 32) * 16; i += kHeadThreads) sx[i] = 0.f;
   __syncthreads();
+  auto group_vals = [&](int it, float (&v)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      if constexpr (F32IN) {
+        const uint32_t w = xr[it][e >> 2][e & 3];
+        v[e] = __uint_as_float(w);
+      } else {
+        v[e] = bf16_to_f32((uint16_t)(xr[it][0][e >> 1] >> (16 * (e & 1))));
+      }
+    }
+  };
+#pragma unroll
+  for (int it = 0; it < XG; it++) {
+    const int i = it * kHeadThreads + tid;
+    if (it * kHeadThreads < total && i < total) {
+      float v[8];
+      group_vals(it, v);
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) m = fmaxf(m, fabsf(v[e]));
+      atomicMax(&s_maxbits[i / ngrp], __float_as_uint(m));
+    }
+  }
+  __syncthreads();
+  if (tid < R) {
+    const float m = __uint_as_float(s_maxbits[tid]);
+    int ex = 0;
+    if (m > 0.f) frexpf(m, &ex);        // m = f * 2^ex, f in [0.5, 1)
+    const int sh = m > 0.f ? 15 - ex : 0;
+    s_scale[tid] = ldexpf(1.f, sh);
+    s_unscale[tid] = ldexpf(1.f, -sh);
+  }
+  __syncthreads();
 
-  // stage binary16 operand (inputs permuted within groups of 8) and block sums
-  const int ngrp = H / 8, total = R * ngrp;
-  for (int base = 0; base < total; base += kHeadThreads) {
+  // stage the binary16 operand (inputs permuted within groups of 8) and the block sums
+#pragma unroll
+  for (int it = 0; it < XG; it++) {
+    const int base = it * kHeadThreads;
+    if (base >= total) break;
     const int i = base + tid;
     const bool ok = i < total;
     const int j = ok ? i / ngrp : 0, u = ok ? i % ngrp : 0;
+    float v[8];
+    group_vals(it, v);
     _Float16 hi[8], lo[8];
     float shi = 0.f, slo = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      const float v = ok ? load_x<F32IN>(a.x, (long)j * H + 8 * u + e) * s_scale[j] : 0.f;
-      hi[e] = (_Float16)v;
-      lo[e] = f32in ? (_Float16)(v - (float)hi[e]) : (_Float16)0.f;
+      const float sv = ok ? v[e] * s_scale[j] : 0.f;
+      hi[e] = (_Float16)sv;
+      lo[e] = F32IN ? (_Float16)(sv - (float)hi[e]) : (_Float16)0.f;
       shi += (float)hi[e];
       slo += (float)lo[e];
     }
@@ -82,61 +170,68 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(HeadArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; e++) { ph[e] = hi[perm_q8(e)]; pl[e] = lo[perm_q8(e)]; }
       *(f16x8*)(xs + (size_t)j * stride + 8 * u) = ph;
-      if (f32in) *(f16x8*)(xs + (size_t)(8 + j) * stride + 8 * u) = pl;
+      if (F32IN) *(f16x8*)(xs + (size_t)(8 + j) * stride + 8 * u) = pl;
       if ((u & 3) == 0) {
         sx[(u >> 2) * 16 + j] = shi;
-        sx[(u >> 2) * 16 + 8 + j] = slo;
+        if (F32IN) sx[(u >> 2) * 16 + 8 + j] = slo;
       }
     }
   }
   __syncthreads();
 
-  const int c = lane & 15, q = lane >> 4;
-  const bool col_ok = (c & 7) < R && (c < 8 || f32in);
-  const int NG = H / 64;    // k-groups of 64 inputs = 2 blocks
+  const bool col_ok = (c & 7) < R && (c < 8 || F32IN);
   float best_v[4];
   int best_i[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) { best_v[i] = -INFINITY; best_i[i] = 0x7FFFFFFF; }
-
-  for (int u = 0; u < kHeadTilesPerWave; u++) {
-    const int tile = (blockIdx.x * 4 + wave) * kHeadTilesPerWave + u;
-    if (tile * 16 >= V) break;
-    const u32x4* cp = (const u32x4*)a.codes + (long)tile * NG * 64 + lane;
-    const uint32_t* mp = (const uint32_t*)a.meta + ((long)tile * NG * 16 + c);  // 2 x u16 per row
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < NG; g++) {
-      const u32x4 cw = cp[(long)g * 64];
-      const uint32_t mw = mp[(long)g * 16];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, mn = acc;
+  int cu_j = 0, cu_g = 0;
+  run_ring<D>(units, [&](auto d_, bool refill) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_)::value;
+    const u32x4 cw = rc[d];
+    const uint32_t mw = rm[d];
+    if (refill) issue(d_);
 #pragma unroll
-      for (int beta = 0; beta < 2; beta++) {
-        const int blk = 2 * g + beta;
-        f16x8 ax = {};
-        if (col_ok) ax = *(const f16x8*)(xs + (size_t)c * stride + blk * 32 + q * 8);
-        const f16x8 bq = q8_to_f16x8(cw[2 * beta], cw[2 * beta + 1]);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 d = mfma_f16(ax, bq, z);
-        const float s = beta ? f16_hi(mw) : f16_lo(mw);
-        const float* sxb = sx + blk * 16 + 4 * q;
+    for (int beta = 0; beta < 2; beta++) {
+      const int blk = 2 * cu_g + beta;
+      f16x8 ax = {};
+      if (col_ok) ax = *(const f16x8*)(xs + (size_t)c * stride + blk * 32 + q * 8);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 dd = mfma_f16(ax, q8_to_f16x8(cw[2 * beta], cw[2 * beta + 1]), z);
+      const float sc = beta ? f16_hi(mw) : f16_lo(mw);
 #pragma unroll
-        for (int i = 0; i < 4; i++) acc[i] = fmaf(s, fmaf(-1152.f, sxb[i], d[i]), acc[i]);
-      }
+      for (int i = 0; i < 4; i++) acc[i] = fmaf(sc, dd[i], acc[i]);
     }
+    // -1152 * scale * Sx of the unit's blocks: lane (k = l/16 < 2) supplies block 2g + k
+    const float am = q < 2 ? sx[(2 * cu_g + q) * 16 + c] : 0.f;
+    const float bm = q == 0 ? -1152.f * f16_lo(mw) : (q == 1 ? -1152.f * f16_hi(mw) : 0.f);
+    mn = mfma_f32x4(am, bm, mn);
+    if (++cu_g == NG) {
+      f32x4 tot;
 #pragma unroll
-    for (int i = 0; i < 4; i++) acc[i] += __shfl_down(acc[i], 32);
-    if (lane < 32) {
-      const int v = tile * 16 + c;
+      for (int i = 0; i < 4; i++) tot[i] = acc[i] + mn[i];
+      if constexpr (F32IN) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int r = 4 * q + i;
-        if (r < R) {
-          const float val = acc[i] * s_unscale[r];
-          if (a.logits) a.logits[(long)r * V + v] = val;
-          if (val > best_v[i] || (val == best_v[i] && v < best_i[i])) { best_v[i] = val; best_i[i] = v; }
+        for (int i = 0; i < 4; i++) tot[i] += __shfl_down(tot[i], 32);
+      }
+      if (lane < 32) {
+        const int v = (gw + cu_j * TW) * 16 + c;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int r = 4 * q + i;
+          if (r < R) {
+            const float val = tot[i] * s_unscale[r];
+            if (a.logits) a.logits[(long)r * V + v] = val;
+            if (val > best_v[i] || (val == best_v[i] && v < best_i[i])) { best_v[i] = val; best_i[i] = v; }
+          }
         }
       }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      mn = acc;
+      cu_g = 0;
+      ++cu_j;
     }
-  }
+  });
   // reduce candidates over the 16 lanes of each row group (columns = vocab)
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -158,16 +253,15 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(HeadArgs a) {
   if (tid < R) {
     float bv = s_bv[0][tid];
     int bi = s_bi[0][tid];
-    for (int w = 1; w < 4; w++)
+    for (int w = 1; w < kHeadWaves; w++)
       if (s_bv[w][tid] > bv || (s_bv[w][tid] == bv && s_bi[w][tid] < bi)) { bv = s_bv[w][tid]; bi = s_bi[w][tid]; }
     a.part_val[(long)blockIdx.x * R + tid] = bv;
     a.part_idx[(long)blockIdx.x * R + tid] = bi;
   }
-
 }
 
 // Per-row argmax over the workgroups' candidates (one workgroup, after k_head).
-__global__ __launch_bounds__(kHeadThreads) void k_head_argmax(HeadArgs a, int nwg) {
+__global__ __launch_bounds__(256) void k_head_argmax(HeadArgs a, int nwg) {
   const int R = a.rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int r = wave; r < R; r += 4) {
@@ -217,24 +311,38 @@ int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p) {
   return (int)hipGetLastError();
 }
 
-int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p) {
-  const size_t lds = head_lds_bytes(a.hidden, a.x_dtype == 0 ? 16 : 8);
+template <bool F32IN, int XG>
+static int launch_head_k(const HeadArgs& a, size_t lds, int nwg, hipStream_t s, const Prof* p) {
   static size_t granted = 64 * 1024;   // raise the dynamic LDS limit once, when needed
   if (lds > granted) {
-    if (int e = (int)hipFuncSetAttribute((const void*)k_head<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
-      return e;
-    if (int e = (int)hipFuncSetAttribute((const void*)k_head<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
+    if (int e = (int)hipFuncSetAttribute((const void*)k_head<F32IN, XG>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds))
       return e;
     granted = lds;
   }
+  launch(k_head<F32IN, XG>, dim3(nwg), dim3(kHeadThreads), lds, s, p, a);
+  return 0;
+}
+
+template <bool F32IN>
+static int launch_head_x(const HeadArgs& a, size_t lds, int nwg, hipStream_t s, const Prof* p) {
+  // activation groups of 8 per thread, all loaded up front
+  const int groups = a.rows * (a.hidden / 8);
+  if (groups <= 4 * kHeadThreads) return launch_head_k<F32IN, 4>(a, lds, nwg, s, p);
+  if (groups <= 8 * kHeadThreads) return launch_head_k<F32IN, 8>(a, lds, nwg, s, p);
+  if (groups <= 16 * kHeadThreads) return launch_head_k<F32IN, 16>(a, lds, nwg, s, p);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p) {
+  const size_t lds = head_lds_bytes(a.hidden, a.x_dtype == 0 ? 16 : 8);
   Prof p0, p1;
   if (p) { p0.start = p->start; p1.stop = p->stop; }
   const int nwg = head_workgroups(a.vocab);
-  if (a.x_dtype == 0)
-    launch(k_head<true>, dim3(nwg), dim3(kHeadThreads), lds, s, p ? &p0 : nullptr, a);
-  else
-    launch(k_head<false>, dim3(nwg), dim3(kHeadThreads), lds, s, p ? &p0 : nullptr, a);
-  launch(k_head_argmax, dim3(1), dim3(kHeadThreads), 0, s, p ? &p1 : nullptr, a, nwg);
+  const int e = a.x_dtype == 0 ? launch_head_x<true>(a, lds, nwg, s, p ? &p0 : nullptr)
+                               : launch_head_x<false>(a, lds, nwg, s, p ? &p0 : nullptr);
+  if (e) return e;
+  launch(k_head_argmax, dim3(1), dim3(256), 0, s, p ? &p1 : nullptr, a, nwg);
   return (int)hipGetLastError();
 }
 

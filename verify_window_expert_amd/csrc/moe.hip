@@ -39,16 +39,9 @@ constexpr int kGuDepth = SW_GU_DEPTH;                // gate/up: units in flight
 #define SW_DN_DEPTH 4
 #endif
 constexpr int kDnDepth = SW_DN_DEPTH;                // down: units in flight per wave
-
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), unrolled: ring
-// slots are then compile-time register arrays.
-template <int N, int I = 0, class Fn>
-__device__ __forceinline__ void static_for(Fn&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
+#ifndef SW_WEIGHT_AUX
+#define SW_WEIGHT_AUX 2                              // weight loads: non-temporal (read once per window;
+#endif                                               // measured faster than plain loads)
 
 // ------------------------------------------------------------ activation operand (LDS)
 // LDS image of the activation operand: rows [nrows][stride] of bf16, inputs permuted
@@ -306,10 +299,10 @@ template <int BITS>
 __device__ __forceinline__ void load_kgroup(KGroup<BITS>& kg, const TileRsrc& r, int g) {
   constexpr int NB = KGroup<BITS>::NB;
   const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
-  kg.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r.codes, lane * 16, g * 1024, 0));
+  kg.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r.codes, lane * 16, g * 1024, SW_WEIGHT_AUX));
 #pragma unroll
   for (int h = 0; h < NB / 4; h++)
-    kg.meta[h] = __builtin_amdgcn_raw_buffer_load_b32(r.meta, (c * NB + 4 * h + q) * 4, g * 16 * NB * 4, 0);
+    kg.meta[h] = __builtin_amdgcn_raw_buffer_load_b32(r.meta, (c * NB + 4 * h + q) * 4, g * 16 * NB * 4, SW_WEIGHT_AUX);
 }
 
 template <int BITS>
@@ -353,24 +346,6 @@ __device__ __forceinline__ void mac_kgroup(const KGroup<BITS>& k0, const KGroup<
     acc0 = mfma_f32x4(sx, f16_hi(k0.meta[h]) - 128.f * f16_lo(k0.meta[h]), acc0);
     if (TWO) acc1 = mfma_f32x4(sx, f16_hi(k1.meta[h]) - 128.f * f16_lo(k1.meta[h]), acc1);
   }
-}
-
-// Units of a wave's work in rounds of DEPTH through the ring (unit u in slot u % DEPTH):
-// full rounds whose refills are all in range, one round whose refills stop at the end,
-// then the remainder. A round has no early exit: an exit inside the round would make the
-// compiler wait for every outstanding load at the loop head.
-template <int DEPTH, class Step>
-__device__ __forceinline__ void run_ring(int units, Step&& step) {
-  int u0 = 0;
-  for (; u0 + 2 * DEPTH <= units; u0 += DEPTH)
-    static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { step(d, true); });
-  if (u0 + DEPTH <= units) {
-    static_for<DEPTH>([&](auto d) __attribute__((always_inline)) { step(d, u0 + d + DEPTH < units); });
-    u0 += DEPTH;
-  }
-  static_for<DEPTH>([&](auto d) __attribute__((always_inline)) {
-    if (u0 + d < units) step(d, false);
-  });
 }
 
 // ------------------------------------------------------------------------ gate / up
