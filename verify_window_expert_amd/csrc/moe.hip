@@ -32,11 +32,11 @@ constexpr int kMaxTopk = 8;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxSlots = kMaxRows * kMaxTopk + 1;   // routed experts a window can use + shared
 #ifndef SW_GU_DEPTH
-#define SW_GU_DEPTH 4
+#define SW_GU_DEPTH 2
 #endif
 constexpr int kGuDepth = SW_GU_DEPTH;                // gate/up: units in flight per wave (ring slots)
 #ifndef SW_DN_DEPTH
-#define SW_DN_DEPTH 4
+#define SW_DN_DEPTH 2
 #endif
 constexpr int kDnDepth = SW_DN_DEPTH;                // down: units in flight per wave
 #ifndef SW_WEIGHT_AUX
