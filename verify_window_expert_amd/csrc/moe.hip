@@ -407,7 +407,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   constexpr int G = 512 / BITS;
   const int NG = H / G;
-  const int grid = gridDim.x;
+  // (the fused layer's last workgroup only writes the routing outputs: the others own
+  // the items)
+  const int grid = ROUTED ? gridDim.x - 1 : gridDim.x;
 
   // the activations (XG groups of 8 per thread) and the tables, all loads at once
   const ActLds l = act_lds(smem, H, F32IN ? 16 : 8);
@@ -418,20 +420,24 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   if constexpr (ROUTED) {
     // the router's partials (requested first) and the activations; then the routing
     // core, which leaves the window's tables in LDS (two candidate experts per lane up
-    // to 128 experts, else four: a branch on the expert count, the same in every wave)
+    // to 128 experts, else four: a branch on the expert count, the same in every wave).
+    // The last workgroup also takes the weights and writes the routing outputs, and has
+    // no items.
+    const bool router = blockIdx.x == gridDim.x - 1;
     if (E <= 2 * kWave) {
       RouteRegs<2> rg;
       route_load<2>(a.route, rg);
       load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
       __builtin_amdgcn_sched_barrier(0);
-      route_select<2>(a.route, rg, rl.v, blockIdx.x == 0);
+      route_select<2>(a.route, rg, rl.v, router);
     } else {
       RouteRegs<4> rg;
       route_load<4>(a.route, rg);
       load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
       __builtin_amdgcn_sched_barrier(0);
-      route_select<4>(a.route, rg, rl.v, blockIdx.x == 0);
+      route_select<4>(a.route, rg, rl.v, router);
     }
+    if (router) return;
     n_active = __builtin_amdgcn_readfirstlane(rl.v.n_active);
   } else {
     load_groups<kGuThreads, XG, F32IN>(xr, a.x, R, H);
@@ -833,8 +839,9 @@ template <int BITS, bool F32IN, int XG, bool ROUTED>
 static int launch_gateup_k(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
   auto kern = k_gateup<BITS, F32IN, XG, ROUTED>;
   if (int e = set_lds<k_gateup<BITS, F32IN, XG, ROUTED>>(lds)) return e;
-  launch(kern, dim3(persistent_grid<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds, items, 1)),
-         dim3(kGuThreads), lds, s, p, a);
+  // the fused layer: one more workgroup, which writes the routing outputs
+  const int grid = persistent_grid<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds, items, 1) + (ROUTED ? 1 : 0);
+  launch(kern, dim3(grid), dim3(kGuThreads), lds, s, p, a);
   return 0;
 }
 

@@ -109,16 +109,20 @@ __device__ __forceinline__ void route_load(const RouteArgs& a, RouteRegs<MU>& g)
 
 // Top-k, softmax and grouping from the loaded partials, by the workgroup's first
 // kRouteCoreThreads threads (all of them must call it). Leaves the tables in s; with
-// `out`, also writes them (and the top-k) to a's outputs. Ends with a barrier.
+// `out`, also the weights, and writes the tables, the top-k and the weights to a's
+// outputs. Ends with a barrier.
 //
-// Wave r handles row r: lane l holds experts MU*l .. MU*l + MU - 1. Top-k takes K rounds;
-// in each, the lanes' best remaining keys are compared on their upper 32 bits (one DPP
-// max), and only when several lanes share the largest upper half are those lanes' whole
-// keys compared. The winner's lane pops it. The softmax shift is the first winner's
-// logit; the denominator (double sum of float exponentials) does not depend on the later
-// rounds. The row's selections go to LDS as a row mask per expert and a weight per (row,
-// expert); waves 0..3 then list the used experts in ascending order with their rows
-// (ballots give every position directly).
+// Wave r handles row r: lane l holds experts MU*l .. MU*l + MU - 1, each as one unsigned
+// 64-bit key (select_key: larger logit first, ties to the lower index; keys are
+// distinct). The k largest keys are those at or above a threshold found by binary search
+// on the keys' upper 32 bits (each step counts the candidates at or above a trial value
+// with ballots), and, only when several keys share the boundary's upper half, by a
+// second search on the lower 32 bits of those. With `out`, each selected key's place in
+// the row's list is the number of selected keys above it; the softmax shift is the
+// largest key's logit and the denominator a double sum of float exponentials. The row's
+// selections go to LDS as a row mask per expert (and a weight per (row, expert)); waves
+// 0..3 then list the used experts in ascending order with their rows (ballots give every
+// position directly).
 template <int MU>
 __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs<MU>& g, RouteLds& s, bool out) {
   const int H = a.hidden, E = a.n_experts, R = a.rows, K = a.top_k;
@@ -141,76 +145,110 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
       for (int c = 8; c < n_hc; c++) sum += a.partials[((long)c * R + r) * E + min(ee, E - 1)];   // hidden > 4096
       const bool ok = ee < E;
       l[u] = ok ? sum + (a.bias ? (double)g.bias[u] : 0.0) : -INFINITY;
-      hk[u] = ok ? select_key(l[u], ee) : 0ull;   // 0: below every real key
+      hk[u] = ok ? select_key(l[u], ee) : 0ull;   // 0: below every real key (whose upper half is > 0)
     }
-    // the lane's keys sorted descending
-    auto cx = [&](int i, int j) {
-      const uint64_t a0 = hk[i], a1 = hk[j];
-      hk[i] = a0 > a1 ? a0 : a1;
-      hk[j] = a0 > a1 ? a1 : a0;
-    };
-    static_assert(MU == 2 || MU == 4, "two or four candidates per lane");
-    if constexpr (MU == 2) {
-      cx(0, 1);
-    } else {
-      cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+    // the threshold on the upper halves: the largest T with at least K upper halves >= T
+    uint32_t hi[MU];
+#pragma unroll
+    for (int u = 0; u < MU; u++) hi[u] = (uint32_t)(hk[u] >> 32);
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; b--) {
+      const uint32_t cand = T | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < MU; u++) cnt += __popcll(__ballot(hi[u] >= cand));
+      if (cnt >= K) T = cand;
     }
-    uint64_t my_key = 0;
-    double lmax = 0.0, z = 0.0;
-    float ex[MU];
-    for (int j = 0; j < K; j++) {
-      const uint32_t hi = (uint32_t)(hk[0] >> 32);
-      const uint32_t bh = wave_max_u32(hi);
-      uint64_t m = __ballot(hi == bh);
-      if (__popcll(m) != 1) {   // equal upper halves: the whole keys of those lanes decide
-        const uint64_t best = wave_max_key(hi == bh ? hk[0] : 0ull);
-        m = __ballot(hk[0] == best);
-      }
-      const int wl = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
-      const uint64_t best = ((uint64_t)__builtin_amdgcn_readlane((int)(uint32_t)(hk[0] >> 32), wl) << 32) |
-                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)hk[0], wl);
-      if (lane == wl) {
-#pragma unroll
-        for (int u = 0; u + 1 < MU; u++) hk[u] = hk[u + 1];
-        hk[MU - 1] = 0;
-      }
-      if (lane == j) my_key = best;
-      if (j == 0) {
-        // the shift: the winner's logit, read from the lane that holds it
-        const int e0 = key_expert(best), u0 = e0 % MU;
-        double lu = l[0];
-#pragma unroll
-        for (int u = 1; u < MU; u++) lu = u == u0 ? l[u] : lu;
-        const uint64_t b = __builtin_bit_cast(uint64_t, lu);
-        lmax = __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), e0 / MU) << 32) |
-                                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, e0 / MU));
-        double zl = 0.0;
-#pragma unroll
-        for (int u = 0; u < MU; u++) {
-          ex[u] = MU * lane + u < E ? exp_nonpos(l[u] - lmax) : 0.f;
-          zl += (double)ex[u];
-        }
-        z = wave_sum(zl);
-      }
-    }
-    // the K weights in parallel (lane j: the j-th winner's exponential from its lane)
-    const int my_e = key_expert(my_key);
-    float e_sel = 0.f;
+    int above = 0, at = 0;
 #pragma unroll
     for (int u = 0; u < MU; u++) {
-      const float v = __shfl(ex[u], (my_e / MU) & 63);
-      if (my_e % MU == u) e_sel = v;
+      above += __popcll(__ballot(hi[u] > T));
+      at += __popcll(__ballot(hi[u] == T));
     }
-    double my_w = (double)e_sel / z;
-    // weights (divided by their sum over the row's k when asked), in selection order
-    if (a.renorm) my_w = my_w / wave_sum(lane < K ? my_w : 0.0);
-    if (lane < K) {
-      if (out) {
-        a.topk_idx[r * K + lane] = my_e;
-        a.topk_w[r * K + lane] = (float)my_w;
+    // several keys share the boundary's upper half: the largest K - above of them by
+    // their lower halves (distinct, since the keys are)
+    uint32_t T2 = 0;
+    if (above + at > K) {
+      const int need = K - above;
+      for (int b = 31; b >= 0; b--) {
+        const uint32_t cand = T2 | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < MU; u++) cnt += __popcll(__ballot(hi[u] == T && (uint32_t)hk[u] >= cand));
+        if (cnt >= need) T2 = cand;
       }
-      s.wt[r][my_e] = (float)my_w;
-      atomicOr(&s.mask[my_e], 1u << r);
+    }
+    bool sel[MU];
+#pragma unroll
+    for (int u = 0; u < MU; u++) sel[u] = hi[u] > T || (hi[u] == T && (uint32_t)hk[u] >= T2);
+
+    if (out) {
+      // each selected key's place: the selected keys above it (K readlane steps over the
+      // selection's ballots)
+      int rank[MU] = {};
+      uint64_t bal[MU];
+#pragma unroll
+      for (int u = 0; u < MU; u++) bal[u] = __ballot(sel[u]);
+#pragma unroll
+      for (int v = 0; v < MU; v++) {
+        uint64_t m = bal[v];
+        while (m) {
+          const int sl = __builtin_ctzll(m);
+          m &= m - 1;
+          const uint64_t kv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(hk[v] >> 32), sl) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)hk[v], sl);
+#pragma unroll
+          for (int u = 0; u < MU; u++) rank[u] += kv > hk[u];
+        }
+      }
+      // the softmax shift: the logit of the largest key
+      int top_lane = 0, top_u = 0;
+#pragma unroll
+      for (int u = 0; u < MU; u++) {
+        const uint64_t b = __ballot(sel[u] && rank[u] == 0);
+        if (b) { top_lane = __builtin_ctzll(b); top_u = u; }
+      }
+      double lu = l[0];
+#pragma unroll
+      for (int u = 1; u < MU; u++) lu = u == top_u ? l[u] : lu;
+      const uint64_t lb = __builtin_bit_cast(uint64_t, lu);
+      const double lmax = __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lb >> 32), top_lane) << 32) |
+                                                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lb, top_lane));
+      float ex[MU];
+      double zl = 0.0;
+#pragma unroll
+      for (int u = 0; u < MU; u++) {
+        ex[u] = MU * lane + u < E ? exp_nonpos(l[u] - lmax) : 0.f;
+        zl += (double)ex[u];
+      }
+      const double z = wave_sum(zl);
+      double w[MU];
+      double wsel = 0.0;
+#pragma unroll
+      for (int u = 0; u < MU; u++) {
+        w[u] = (double)ex[u] / z;
+        if (sel[u]) wsel += w[u];
+      }
+      // weights (divided by their sum over the row's k when asked)
+      if (a.renorm) {
+        const double tot = wave_sum(wsel);
+#pragma unroll
+        for (int u = 0; u < MU; u++) w[u] = w[u] / tot;
+      }
+#pragma unroll
+      for (int u = 0; u < MU; u++) {
+        if (sel[u]) {
+          const int e = MU * lane + u;
+          a.topk_idx[r * K + rank[u]] = e;
+          a.topk_w[r * K + rank[u]] = (float)w[u];
+          s.wt[r][e] = (float)w[u];
+          atomicOr(&s.mask[e], 1u << r);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < MU; u++)
+        if (sel[u]) atomicOr(&s.mask[MU * lane + u], 1u << r);
     }
   }
   __syncthreads();
