@@ -34,12 +34,12 @@ def layer_for(cfg, layer=0):
     return _layers[key]
 
 
-def check_window(cfg, window=0, renorm=False, residual=False, x=None, x_next=False, ties=False):
+def check_window(cfg, window=0, renorm=False, residual=False, x=None, x_next=False, ties=False, layer=False):
     L, dl, mats = layer_for(cfg)
     x = synth.make_window(cfg, window) if x is None else x
     print(f"[parity] cid={cfg.cid} H={cfg.hidden} F={cfg.ffn} E={cfg.experts} k={cfg.top_k} bits={cfg.bits} "
-          f"R={x.shape[0]} window={window} renorm={renorm} residual={residual}", flush=True)
-    gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next)
+          f"R={x.shape[0]} window={window} renorm={renorm} residual={residual} layer={layer}", flush=True)
+    gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next, layer=layer)
     orc, oout, oxn = oracle_window(L, mats, x, cfg, renorm, residual, x_next)
     # exact ties (equal logits) are decided identically by index; near-ties are not
     # well-posed across summation orders, so a seed must not produce them
@@ -96,27 +96,31 @@ def test_x_next_is_bf16_of_output():
 # --------------------------------------------------------------------- shapes and edges
 
 @pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_every_row_count(rows):
+@pytest.mark.parametrize("layer", [False, True])
+def test_every_row_count(rows, layer):
     cfg = synth.config(0, rows=rows, top_k=3, experts=13)
-    check_window(cfg, 5)
+    check_window(cfg, 5, layer=layer)
 
 
-def test_ragged_shapes():
+@pytest.mark.parametrize("layer", [False, True])
+def test_ragged_shapes(layer):
     """Expert count not a multiple of the router's 4 experts per workgroup, hidden not a
     multiple of its 512-input chunk, several output ranges, 2-bit."""
-    check_window(synth.config(0, hidden=640, ffn=384, experts=13, top_k=5, rows=7), 0)
-    check_window(synth.config(0, hidden=768, ffn=512, experts=10, top_k=4, rows=5, bits=2, x_dtype="bf16"), 1)
+    check_window(synth.config(0, hidden=640, ffn=384, experts=13, top_k=5, rows=7), 0, layer=layer)
+    check_window(synth.config(0, hidden=768, ffn=512, experts=10, top_k=4, rows=5, bits=2, x_dtype="bf16"), 1, layer=layer)
 
 
-def test_all_rows_share_experts():
+@pytest.mark.parametrize("layer", [False, True])
+def test_all_rows_share_experts(layer):
     cfg = synth.config(0, rows=8, top_k=4)
     x = np.repeat(synth.make_window(cfg, 0)[:1], 8, axis=0)
-    gr, gout, _, _, _, _ = check_window(cfg, x=x)
+    gr, gout, _, _, _, _ = check_window(cfg, x=x, layer=layer)
     assert gr["n_active"] == 4 + 1
     assert np.all(gout == gout[0])
 
 
-def test_disjoint_rows():
+@pytest.mark.parametrize("layer", [False, True])
+def test_disjoint_rows(layer):
     cfg = synth.config(0, rows=8, top_k=2, experts=16)
     L, dl, mats = layer_for(cfg)
     x = np.zeros((8, cfg.hidden), np.float32)
@@ -124,27 +128,37 @@ def test_disjoint_rows():
     G = L.gate_w.astype(np.float64)
     for r in range(8):
         x[r] = (40.0 * (G[2 * r] + G[2 * r + 1]) / np.linalg.norm(G[2 * r] + G[2 * r + 1]) ** 2).astype(np.float32)
-    gr, _, _, _, _, _ = check_window(cfg, x=x)
+    gr, _, _, _, _, _ = check_window(cfg, x=x, layer=layer)
     assert gr["n_active"] == 16 + 1
     assert sorted(gr["topk_idx"].ravel().tolist()) == list(range(16))
 
 
-def test_k_equals_e_full_mixture():
-    check_window(synth.config(0, experts=8, top_k=8, rows=3), 0, renorm=True)
+@pytest.mark.parametrize("layer", [False, True])
+def test_k_equals_e_full_mixture(layer):
+    check_window(synth.config(0, experts=8, top_k=8, rows=3), 0, renorm=True, layer=layer)
 
 
-def test_zero_rows():
+@pytest.mark.parametrize("layer", [False, True])
+def test_zero_rows(layer):
     cfg = synth.config(0, rows=3)
     x = synth.make_window(cfg, 0)
     x[1] = 0.0
-    gr, gout, oout, _, _, _ = check_window(cfg, x=x, ties=True)
+    gr, gout, oout, _, _, _ = check_window(cfg, x=x, ties=True, layer=layer)
     assert list(gr["topk_idx"][1]) == list(range(cfg.top_k))   # equal logits: lowest indices
     assert np.all(gout[1] == 0.0)
 
 
-def test_max_limits():
+@pytest.mark.parametrize("layer", [False, True])
+def test_max_limits(layer):
     """rows 8, k 8, 256 experts (the ABI's maxima), reduced width."""
-    check_window(synth.config(4, hidden=1024, ffn=256, rows=8), 0)
+    check_window(synth.config(4, hidden=1024, ffn=256, rows=8), 0, layer=layer)
+
+
+@pytest.mark.parametrize("layer", [False, True])
+def test_hidden_beyond_eight_router_chunks(layer):
+    """hidden 4608: nine 512-input router chunks, more than the routing core keeps in
+    registers (the rest are read where they are added)."""
+    check_window(synth.config(1, hidden=4608, ffn=256, experts=16, top_k=4, rows=6), 0, layer=layer)
 
 
 # --------------------------------------------------------------------- invariance
