@@ -8,7 +8,7 @@ gate/up whose workgroups take the routing themselves, then down and combine); --
 runs strata_window_route and then strata_window_moe instead. The default
 workload is the 8-row window (4 slots x token + MTP proposal, Zipf(1.1) router prior,
 correlated pairs) of a 2048-hidden / 768-ffn / 128-expert top-8 layer with 4-bit block
-quantization. --config 3 runs the 24-layer stack with the 8-bit head instead (a step is
+quantization. --workload stack24_head runs the 24-layer stack with the 8-bit head instead (a step is
 then one window through all 24 layers and the head).
 
 Timing: K steps are captured into one HIP graph (inputs resident in HBM) and replayed
@@ -42,8 +42,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=32)
-    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
-    p.add_argument("--rows", type=int, default=None, help="window rows (config 4 sweep)")
+    p.add_argument("--workload", default="four_slots_mtp_zipf",
+                   choices=["two_slots_mtp", "four_slots_mtp_zipf", "stack24_head", "e256_2bit"])
+    p.add_argument("--rows", type=int, default=None, help="window rows (e256_2bit row sweep)")
     p.add_argument("--layers", type=int, default=16, help="layer instances to cycle through")
     p.add_argument("--windows", type=int, default=256, help="distinct activation windows")
     p.add_argument("--prof-steps", type=int, default=512, help="eager steps timed per kernel")
@@ -274,9 +275,9 @@ def main():
     if args.calibrate_copy_mib > 0:
         calibration_copy(torch, args.calibrate_copy_mib)
 
-    if args.config == 3:
+    if args.workload == "stack24_head":
         return bench_stack(args, torch, synth, sw, DevLayer, to_dev_x)
-    cfg = synth.config(args.config, **({"rows": args.rows} if args.rows else {}))
+    cfg = synth.config(args.workload, **({"rows": args.rows} if args.rows else {}))
     K, W = args.steps, args.warmup
     NF = max(1, args.inflight)
     st = Steps(cfg, args.layers, args.windows, max(K, args.prof_steps), sw, torch, synth, DevLayer, to_dev_x, NF,
@@ -340,7 +341,7 @@ def main():
     # dominant kernel: gate/up (two thirds of the window's bytes)
     gu_bytes = [(u + 1) * 2 * F * H * bpw(cfg.bits) for u in U_prof]
     gu_gbs = sum(gu_bytes) / (sum(d_gu) * 1e-3) / 1e9
-    traffic = counter_traffic("k_gateup", f"config{cfg.cid}")
+    traffic = counter_traffic("k_gateup", cfg.name)
     roof = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": ("k_gateup (fused {}-bit dequant gate/up matvec + SwiGLU{})".format(
@@ -353,17 +354,17 @@ def main():
         log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget)")
         cpu = cpu_baseline(cfg, st.host_layer0, args.cpu_seconds)
 
-    workload = {2: "one MoE layer, 8-row verify window (4 slots x token+MTP proposal, Zipf(1.1) router prior, "
+    workload = {"four_slots_mtp_zipf": "one MoE layer, 8-row verify window (4 slots x token+MTP proposal, Zipf(1.1) router prior, "
                    "correlated pairs), hidden 2048, ffn 768, 128 experts top-8 + shared, 4-bit blocks of 32",
-                1: "one MoE layer, 4-row verify window (2 slots with MTP), hidden 2048, ffn 768, 128 experts top-8 "
+                "two_slots_mtp": "one MoE layer, 4-row verify window (2 slots with MTP), hidden 2048, ffn 768, 128 experts top-8 "
                    "+ shared, 4-bit blocks of 32",
-                4: f"one MoE layer, {R}-row window, hidden 4096, ffn 1024, 256 experts top-8 + shared, 2-bit "
-                   "blocks of 32"}[cfg.cid]
+                "e256_2bit": f"one MoE layer, {R}-row window, hidden 4096, ffn 1024, 256 experts top-8 + shared, 2-bit "
+                   "blocks of 32"}[cfg.name]
     line = {
         "metric": METRIC, "value": round(rows_s, 1), "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_total / K, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": workload, "config_id": cfg.cid, "rows": R, "hidden": H, "ffn": F, "experts": E,
+        "config": {"workload": workload, "name": cfg.name, "rows": R, "hidden": H, "ffn": F, "experts": E,
                    "top_k": cfg.top_k, "bits": cfg.bits, "layer_instances": args.layers,
                    "windows_in_flight": NF, "path": args.path},
         "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
@@ -379,7 +380,7 @@ def main():
 
 def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
     """24 layers + head per step (the layer-stack workload)."""
-    cfg = synth.config(3)
+    cfg = synth.config("stack24_head")
     K, W = min(args.steps, 256), min(args.warmup, 8)
     R, H, F, E, k = cfg.rows, cfg.hidden, cfg.ffn, cfg.experts, cfg.top_k
     t0 = time.time()
@@ -453,7 +454,7 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "24 MoE layers (hidden 2048, ffn 768, 128 experts top-8 + shared, 4-bit) with "
                                    "residual, then an 8-bit head of vocab 151936 with argmax, 8-row window",
-                       "config_id": 3, "path": args.path},
+                       "name": "stack24_head", "path": args.path},
             "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
             "kernel_us": {"head": round(head_us, 3)},
             "roofline": {"bound": "hbm", "achieved": round(b_h / (head_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,

@@ -6,15 +6,17 @@ and both the HIP path's tests/benchmark and the CPU oracle take their inputs fro
 
 The pages measure whole models whose weights and prompts are not available (Strata
 docs/BATCHING.md, "Measured": UD-Q4_K_XL, Q2_0, IQ3_S models and the benchmark's own
-prompts). These generators stand in for them with the shapes of five configurations:
+prompts). These generators stand in for them with the shapes of five workloads:
 
-  cid  hidden  ffn   experts  top_k  bits  rows        activations
-  0    256     128   16       2      4     2           float32, independent
-  1    2048    768   128      8      4     4           bf16, independent, uniform routing
-  2    2048    768   128      8      4     8           bf16, 4 (token, proposal) pairs with
-                                                       cosine ~0.9, Zipf(1.1) router prior
-  3    24 layers of cid 1's shape, 8 rows, then an 8-bit head of vocab 151936
-  4    4096    1024  256      8      2     1, 2, 4, 8  bf16, independent, uniform routing
+  name                 hidden  ffn   experts  top_k  bits  rows        activations
+  small_f32            256     128   16       2      4     2           float32, independent
+  two_slots_mtp        2048    768   128      8      4     4           bf16, independent, uniform routing
+  four_slots_mtp_zipf  2048    768   128      8      4     8           bf16, 4 (token, proposal) pairs with
+                                                                       cosine ~0.9, Zipf(1.1) router prior
+  stack24_head         24 layers of two_slots_mtp's shape, 8 rows, then an 8-bit head of vocab 151936
+  e256_2bit            4096    1024  256      8      2     1, 2, 4, 8  bf16, independent, uniform routing
+
+Each workload's `seed` keys its random streams.
 
 Value recipe (not from the pages; chosen so activations stay O(1) through 24 layers and
 the dequantised weights are exact in float32):
@@ -27,8 +29,8 @@ the dequantised weights are exact in float32):
           over 24 layers (the models on the pages normalise each layer's input; that
           dense part is outside this layer)
   min:    binary16( -scale * (2^bits - 1) / 2 )      (affine formats only)
-  router: float32 N(0, 0.02);  bias (cid 2): -1.1 * ln(rank_e), rank a random permutation
-  x:      N(0, 1); cid 2 rows (2s, 2s+1): x_p = 0.9 x_t + sqrt(0.19) z; then bf16 (RNE)
+  router: float32 N(0, 0.02);  bias (Zipf workloads): -1.1 * ln(rank_e), rank a random permutation
+  x:      N(0, 1); paired workloads' rows (2s, 2s+1): x_p = 0.9 x_t + sqrt(0.19) z; then bf16 (RNE)
 """
 from dataclasses import dataclass, replace
 
@@ -37,7 +39,8 @@ import numpy as np
 
 @dataclass(frozen=True)
 class Config:
-    cid: int
+    name: str
+    seed: int
     hidden: int
     ffn: int
     experts: int
@@ -52,18 +55,18 @@ class Config:
     head_bits: int = 8
 
 
-CONFIGS = {
-    0: Config(0, 256, 128, 16, 2, 4, 2, "f32"),
-    1: Config(1, 2048, 768, 128, 8, 4, 4, "bf16"),
-    2: Config(2, 2048, 768, 128, 8, 4, 8, "bf16", zipf=True, pairs=True),
-    3: Config(3, 2048, 768, 128, 8, 4, 8, "bf16", layers=24, vocab=151936),
-    4: Config(4, 4096, 1024, 256, 8, 2, 8, "bf16"),
-}
-CONFIG4_ROWS = (1, 2, 4, 8)
+CONFIGS = {c.name: c for c in (
+    Config("small_f32", 0, 256, 128, 16, 2, 4, 2, "f32"),
+    Config("two_slots_mtp", 1, 2048, 768, 128, 8, 4, 4, "bf16"),
+    Config("four_slots_mtp_zipf", 2, 2048, 768, 128, 8, 4, 8, "bf16", zipf=True, pairs=True),
+    Config("stack24_head", 3, 2048, 768, 128, 8, 4, 8, "bf16", layers=24, vocab=151936),
+    Config("e256_2bit", 4, 4096, 1024, 256, 8, 2, 8, "bf16"),
+)}
+E256_ROWS = (1, 2, 4, 8)
 
 
-def config(cid, **over):
-    c = CONFIGS[cid]
+def config(name, **over):
+    c = CONFIGS[name]
     return replace(c, **over) if over else c
 
 
@@ -126,10 +129,10 @@ class Layer:
 def make_router(cfg, layer=0):
     """Router of layer instance `layer`: (gate_w [E, H] float32, bias [E] float32 or None)."""
     E, H = cfg.experts, cfg.hidden
-    gate_w = _rng(cfg.cid, 1, layer, 0).normal(0.0, 0.02, size=(E, H)).astype(np.float32)
+    gate_w = _rng(cfg.seed, 1, layer, 0).normal(0.0, 0.02, size=(E, H)).astype(np.float32)
     bias = None
     if cfg.zipf:
-        rank = _rng(cfg.cid, 1, layer, 3).permutation(E) + 1
+        rank = _rng(cfg.seed, 1, layer, 3).permutation(E) + 1
         bias = (-1.1 * np.log(rank)).astype(np.float32)
     return gate_w, bias
 
@@ -138,7 +141,7 @@ def make_layer(cfg, layer=0):
     """Weights of MoE layer instance `layer` of configuration `cfg`."""
     E, H, F, b = cfg.experts, cfg.hidden, cfg.ffn, cfg.bits
     gate_w, bias = make_router(cfg, layer)
-    r_exp, r_sh = _rng(cfg.cid, 1, layer, 1), _rng(cfg.cid, 1, layer, 2)
+    r_exp, r_sh = _rng(cfg.seed, 1, layer, 1), _rng(cfg.seed, 1, layer, 2)
     g_down = 0.25 if cfg.layers > 1 else 1.0   # the stack's down gain (module docstring)
     gate = qmatrix(r_exp, E, F, H, b)
     up = qmatrix(r_exp, E, F, H, b)
@@ -151,13 +154,13 @@ def make_layer(cfg, layer=0):
 
 def make_head(cfg):
     """8-bit head [vocab, hidden]: (codes [1, ...], meta [1, ...])."""
-    return qmatrix(_rng(cfg.cid, 2), 1, cfg.vocab, cfg.hidden, cfg.head_bits)
+    return qmatrix(_rng(cfg.seed, 2), 1, cfg.vocab, cfg.hidden, cfg.head_bits)
 
 
 def make_window(cfg, window=0, rows=None):
     """Activations of one window: float32 [R, H] (x_dtype f32) or bf16 bits uint16."""
     R = cfg.rows if rows is None else rows
-    rng = _rng(cfg.cid, 3, window)
+    rng = _rng(cfg.seed, 3, window)
     x = rng.standard_normal((R, cfg.hidden))
     if cfg.pairs:
         for s in range(R // 2):

@@ -48,8 +48,8 @@ def test_abi_version(sw):
 
 def test_workspace_sizes(sw):
     L = sw.library()
-    for cid in (0, 1, 2, 4):
-        c = synth.config(cid)
+    for name in ("small_f32", "two_slots_mtp", "four_slots_mtp_zipf", "e256_2bit"):
+        c = synth.config(name)
         r = L.strata_window_workspace(0, c.rows, c.hidden, c.ffn, c.experts, c.top_k, 0)
         m = L.strata_window_workspace(1, c.rows, c.hidden, c.ffn, c.experts, c.top_k, 0)
         assert r >= sw.WS_COUNTER_BYTES + 8 * c.rows * c.experts
@@ -161,8 +161,8 @@ def test_window_limits_from_pages(sw):
     assert g["rows_per_slot_with_batch_mtp"] * g["max_slots_per_window_with_batch_mtp"] == sw.MAX_ROWS
     assert call_route(sw, rows=g["max_rows_per_window"] + 1) == sw.STRATA_EINVAL
     # the synthetic workloads: two MTP slots = 4 rows, four MTP slots = 8 rows
-    assert synth.config(1).rows == 2 * g["rows_per_slot_with_batch_mtp"] == g["workloads"]["two_slots_mtp"]
-    assert synth.config(2).rows == 4 * g["rows_per_slot_with_batch_mtp"] == g["workloads"]["four_slots_mtp"]
+    assert synth.config("two_slots_mtp").rows == 2 * g["rows_per_slot_with_batch_mtp"] == g["workloads"]["two_slots_mtp"]
+    assert synth.config("four_slots_mtp_zipf").rows == 4 * g["rows_per_slot_with_batch_mtp"] == g["workloads"]["four_slots_mtp"]
 
 
 def test_accept_rejects(sw):

@@ -47,7 +47,7 @@ def test_accept_after_gpu_head():
     """The head's argmax on the GPU feeds the accept step: slots 0 and 2 propose the token
     row's argmax (kept, with the proposal row's argmax as bonus), slots 1 and 3 a wrong
     token (one token each)."""
-    cfg = synth.config(3, vocab=4096)
+    cfg = synth.config("stack24_head", vocab=4096)
     x = synth.make_window(cfg, 3)
     codes, meta = synth.make_head(cfg)
     hq = sw.upload_qmat(codes, meta, cfg.vocab, cfg.hidden, 8)

@@ -40,18 +40,18 @@ def head_check(cfg, x, window_label):
 
 
 def test_head_small_bf16():
-    cfg = synth.config(3, vocab=4096)
+    cfg = synth.config("stack24_head", vocab=4096)
     print("head rel err", head_check(cfg, synth.make_window(cfg, 0), "small"))
 
 
 def test_head_small_f32_ragged_rows():
-    cfg = synth.config(0, vocab=1040, hidden=256, rows=5)
+    cfg = synth.config("small_f32", vocab=1040, hidden=256, rows=5)
     head_check(cfg, synth.make_window(cfg, 1), "f32")
 
 
 def test_head_large_magnitudes():
     """Rows scaled by 2^20 and 2^-20 stay exact through the per-row power-of-two scaling."""
-    cfg = synth.config(3, vocab=2048, rows=3)
+    cfg = synth.config("stack24_head", vocab=2048, rows=3)
     x = synth.bf16_bits_to_f32(synth.make_window(cfg, 2))
     x[0] *= 2.0 ** 20
     x[2] *= 2.0 ** -20
@@ -59,7 +59,7 @@ def test_head_large_magnitudes():
 
 
 def test_head_full_vocab():
-    cfg = synth.config(3)
+    cfg = synth.config("stack24_head")
     print("head full rel err", head_check(cfg, synth.make_window(cfg, 0), "full"))
 
 
@@ -67,7 +67,7 @@ def test_layer_stack_teacher_forced():
     """24 layers back to back on the GPU (route, experts with residual, bf16 x_next feeds
     the next layer); every layer is checked against the oracle given the GPU's own input
     to that layer; then the head runs on the last layer's output."""
-    cfg = synth.config(3)
+    cfg = synth.config("stack24_head")
     x = synth.make_window(cfg, 0)
     xd = to_dev_x(x)
     worst = 0.0

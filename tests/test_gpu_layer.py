@@ -31,7 +31,7 @@ def layer_for(cfg):
 def check(cfg, window=0, renorm=False, residual=False, x_next=False):
     L, dl, mats = layer_for(cfg)
     x = synth.make_window(cfg, window)
-    print(f"[layer] cid={cfg.cid} H={cfg.hidden} E={cfg.experts} bits={cfg.bits} R={x.shape[0]} "
+    print(f"[layer] {cfg.name} H={cfg.hidden} E={cfg.experts} bits={cfg.bits} R={x.shape[0]} "
           f"window={window} renorm={renorm} residual={residual}", flush=True)
     gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next, layer=True)
     orc, oout, oxn = oracle_window(L, mats, x, cfg, renorm, residual, x_next)
@@ -43,34 +43,34 @@ def check(cfg, window=0, renorm=False, residual=False, x_next=False):
 
 
 @pytest.mark.parametrize("window", [0, 1])
-def test_layer_config0(window):
-    check(synth.config(0), window)
+def test_layer_small_f32(window):
+    check(synth.config("small_f32"), window)
 
 
-def test_layer_config0_renorm_residual_x_next():
-    _, _, _, gout, gxn, oxn = check(synth.config(0), 2, renorm=True, residual=True, x_next=True)
+def test_layer_small_f32_renorm_residual_x_next():
+    _, _, _, gout, gxn, oxn = check(synth.config("small_f32"), 2, renorm=True, residual=True, x_next=True)
     # x_next is the bf16 rounding of the GPU's own output
     want = (np.frombuffer(np.ascontiguousarray(gout, np.float32).tobytes(), np.uint32))
     rne = ((want + 0x7FFF + ((want >> 16) & 1)) >> 16).astype(np.uint16)
     np.testing.assert_array_equal(gxn.ravel(), rne)
 
 
-def test_layer_config1():
-    check(synth.config(1), 0)
+def test_layer_two_slots_mtp():
+    check(synth.config("two_slots_mtp"), 0)
 
 
 @pytest.mark.parametrize("window", [0, 1, 2])
-def test_layer_config2(window):
-    check(synth.config(2), window)
+def test_layer_four_slots_mtp_zipf(window):
+    check(synth.config("four_slots_mtp_zipf"), window)
 
 
-@pytest.mark.parametrize("rows", synth.CONFIG4_ROWS)
-def test_layer_config4_rows(rows):
-    check(synth.config(4, rows=rows), 0)
+@pytest.mark.parametrize("rows", synth.E256_ROWS)
+def test_layer_e256_2bit_rows(rows):
+    check(synth.config("e256_2bit", rows=rows), 0)
 
 
 def test_layer_row_equals_row_alone_bitwise():
-    cfg = synth.config(2)
+    cfg = synth.config("four_slots_mtp_zipf")
     dl, x, _, gout, _, _ = check(cfg, 3)
     for r in range(x.shape[0]):
         print(f"[layer] row {r} alone", flush=True)
@@ -79,7 +79,7 @@ def test_layer_row_equals_row_alone_bitwise():
 
 
 def test_layer_matches_two_call_path():
-    cfg = synth.config(2)
+    cfg = synth.config("four_slots_mtp_zipf")
     L, dl, _ = layer_for(cfg)
     xd = to_dev_x(synth.make_window(cfg, 5))
     print("[layer] against route + moe", flush=True)

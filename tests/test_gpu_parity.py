@@ -37,7 +37,7 @@ def layer_for(cfg, layer=0):
 def check_window(cfg, window=0, renorm=False, residual=False, x=None, x_next=False, ties=False, layer=False):
     L, dl, mats = layer_for(cfg)
     x = synth.make_window(cfg, window) if x is None else x
-    print(f"[parity] cid={cfg.cid} H={cfg.hidden} F={cfg.ffn} E={cfg.experts} k={cfg.top_k} bits={cfg.bits} "
+    print(f"[parity] {cfg.name} H={cfg.hidden} F={cfg.ffn} E={cfg.experts} k={cfg.top_k} bits={cfg.bits} "
           f"R={x.shape[0]} window={window} renorm={renorm} residual={residual} layer={layer}", flush=True)
     gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next, layer=layer)
     orc, oout, oxn = oracle_window(L, mats, x, cfg, renorm, residual, x_next)
@@ -54,34 +54,34 @@ def check_window(cfg, window=0, renorm=False, residual=False, x=None, x_next=Fal
 # --------------------------------------------------------------------- the five configs
 
 @pytest.mark.parametrize("window", [0, 1])
-def test_config0_tiny(window):
-    check_window(synth.config(0), window)
+def test_small_f32(window):
+    check_window(synth.config("small_f32"), window)
 
 
-def test_config0_renorm_residual():
-    check_window(synth.config(0), 2, renorm=True, residual=True)
+def test_small_f32_renorm_residual():
+    check_window(synth.config("small_f32"), 2, renorm=True, residual=True)
 
 
 @pytest.mark.parametrize("window", [0, 1])
-def test_config1_four_rows(window):
-    _, _, _, err, _, _ = check_window(synth.config(1), window)
-    print("config1 rel err", err)
+def test_two_slots_mtp(window):
+    _, _, _, err, _, _ = check_window(synth.config("two_slots_mtp"), window)
+    print("two_slots_mtp rel err", err)
 
 
 @pytest.mark.parametrize("window", [0, 1, 2])
-def test_config2_eight_rows_zipf_pairs(window):
-    _, _, _, err, _, _ = check_window(synth.config(2), window)
-    print("config2 rel err", err)
+def test_four_slots_mtp_zipf(window):
+    _, _, _, err, _, _ = check_window(synth.config("four_slots_mtp_zipf"), window)
+    print("four_slots_mtp_zipf rel err", err)
 
 
-@pytest.mark.parametrize("rows", synth.CONFIG4_ROWS)
-def test_config4_two_bit_row_sweep(rows):
-    cfg = synth.config(4, rows=rows)
+@pytest.mark.parametrize("rows", synth.E256_ROWS)
+def test_e256_2bit_row_sweep(rows):
+    cfg = synth.config("e256_2bit", rows=rows)
     check_window(cfg, 0)
 
 
 def test_x_next_is_bf16_of_output():
-    cfg = synth.config(1)
+    cfg = synth.config("two_slots_mtp")
     _, gout, oout, _, gxn, oxn = check_window(cfg, 3, residual=True, x_next=True)
     gx = synth.bf16_bits_to_f32(gxn)
     # x_next is the bf16 rounding of the GPU's own output
@@ -98,7 +98,7 @@ def test_x_next_is_bf16_of_output():
 @pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("layer", [False, True])
 def test_every_row_count(rows, layer):
-    cfg = synth.config(0, rows=rows, top_k=3, experts=13)
+    cfg = synth.config("small_f32", rows=rows, top_k=3, experts=13)
     check_window(cfg, 5, layer=layer)
 
 
@@ -106,13 +106,13 @@ def test_every_row_count(rows, layer):
 def test_ragged_shapes(layer):
     """Expert count not a multiple of the router's 4 experts per workgroup, hidden not a
     multiple of its 512-input chunk, several output ranges, 2-bit."""
-    check_window(synth.config(0, hidden=640, ffn=384, experts=13, top_k=5, rows=7), 0, layer=layer)
-    check_window(synth.config(0, hidden=768, ffn=512, experts=10, top_k=4, rows=5, bits=2, x_dtype="bf16"), 1, layer=layer)
+    check_window(synth.config("small_f32", hidden=640, ffn=384, experts=13, top_k=5, rows=7), 0, layer=layer)
+    check_window(synth.config("small_f32", hidden=768, ffn=512, experts=10, top_k=4, rows=5, bits=2, x_dtype="bf16"), 1, layer=layer)
 
 
 @pytest.mark.parametrize("layer", [False, True])
 def test_all_rows_share_experts(layer):
-    cfg = synth.config(0, rows=8, top_k=4)
+    cfg = synth.config("small_f32", rows=8, top_k=4)
     x = np.repeat(synth.make_window(cfg, 0)[:1], 8, axis=0)
     gr, gout, _, _, _, _ = check_window(cfg, x=x, layer=layer)
     assert gr["n_active"] == 4 + 1
@@ -121,7 +121,7 @@ def test_all_rows_share_experts(layer):
 
 @pytest.mark.parametrize("layer", [False, True])
 def test_disjoint_rows(layer):
-    cfg = synth.config(0, rows=8, top_k=2, experts=16)
+    cfg = synth.config("small_f32", rows=8, top_k=2, experts=16)
     L, dl, mats = layer_for(cfg)
     x = np.zeros((8, cfg.hidden), np.float32)
     # rows aligned with pairs of router rows so every row picks its own pair of experts
@@ -135,12 +135,12 @@ def test_disjoint_rows(layer):
 
 @pytest.mark.parametrize("layer", [False, True])
 def test_k_equals_e_full_mixture(layer):
-    check_window(synth.config(0, experts=8, top_k=8, rows=3), 0, renorm=True, layer=layer)
+    check_window(synth.config("small_f32", experts=8, top_k=8, rows=3), 0, renorm=True, layer=layer)
 
 
 @pytest.mark.parametrize("layer", [False, True])
 def test_zero_rows(layer):
-    cfg = synth.config(0, rows=3)
+    cfg = synth.config("small_f32", rows=3)
     x = synth.make_window(cfg, 0)
     x[1] = 0.0
     gr, gout, oout, _, _, _ = check_window(cfg, x=x, ties=True, layer=layer)
@@ -151,23 +151,23 @@ def test_zero_rows(layer):
 @pytest.mark.parametrize("layer", [False, True])
 def test_max_limits(layer):
     """rows 8, k 8, 256 experts (the ABI's maxima), reduced width."""
-    check_window(synth.config(4, hidden=1024, ffn=256, rows=8), 0, layer=layer)
+    check_window(synth.config("e256_2bit", hidden=1024, ffn=256, rows=8), 0, layer=layer)
 
 
 @pytest.mark.parametrize("layer", [False, True])
 def test_hidden_beyond_eight_router_chunks(layer):
     """hidden 4608: nine 512-input router chunks, more than the routing core keeps in
     registers (the rest are read where they are added)."""
-    check_window(synth.config(1, hidden=4608, ffn=256, experts=16, top_k=4, rows=6), 0, layer=layer)
+    check_window(synth.config("two_slots_mtp", hidden=4608, ffn=256, experts=16, top_k=4, rows=6), 0, layer=layer)
 
 
 # --------------------------------------------------------------------- invariance
 
-@pytest.mark.parametrize("cid", [2, 4])
-def test_window_row_equals_row_alone_bitwise(cid):
+@pytest.mark.parametrize("name", ["four_slots_mtp_zipf", "e256_2bit"])
+def test_window_row_equals_row_alone_bitwise(name):
     """Strata docs/BATCHING.md, "Exactness": a batch row's arithmetic is the single-token
     window's. Each row of a full window equals that row run as a 1-row window, bit for bit."""
-    cfg = synth.config(cid)
+    cfg = synth.config(name)
     L, dl, mats = layer_for(cfg)
     x = synth.make_window(cfg, 7)
     gr, gout, _ = gpu_window(dl, to_dev_x(x), cfg.top_k)
@@ -178,7 +178,7 @@ def test_window_row_equals_row_alone_bitwise(cid):
 
 
 def test_run_to_run_deterministic():
-    cfg = synth.config(2)
+    cfg = synth.config("four_slots_mtp_zipf")
     L, dl, mats = layer_for(cfg)
     xd = to_dev_x(synth.make_window(cfg, 4))
     ref = gpu_window(dl, xd, cfg.top_k)[1]
@@ -189,7 +189,7 @@ def test_run_to_run_deterministic():
 def test_workspace_reuse_across_shapes():
     """One workspace, filled with garbage first (it needs no initialisation), serves
     windows of different row counts back to back."""
-    cfg = synth.config(2)
+    cfg = synth.config("four_slots_mtp_zipf")
     L, dl, mats = layer_for(cfg)
     ws_r = sw.workspace(sw.workspace_bytes(0, 8, cfg.hidden, n_experts=cfg.experts)).fill_(0xA5)
     ws_m = sw.workspace(sw.workspace_bytes(1, 8, cfg.hidden, cfg.ffn, cfg.experts, cfg.top_k)).fill_(0xFF)

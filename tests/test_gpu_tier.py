@@ -60,7 +60,7 @@ def test_tier_sequence_matches_oracle(E, decay, every, max_swaps, gain):
 
 def test_tier_counts_from_gpu_routing():
     """The routing output of a config-2 window (Zipf prior, 8 rows) feeds the counts."""
-    cfg = synth.config(2)
+    cfg = synth.config("four_slots_mtp_zipf")
     L = synth.make_layer(cfg, 0)
     dl = DevLayer(L, cfg)
     counts_d = torch.zeros(cfg.experts, dtype=torch.float32, device="cuda")

@@ -96,7 +96,7 @@ def test_dequant_closed_form_every_code(oracle_lib, bits):
 
 def test_generated_weights_are_exact_in_float32(oracle_lib):
     """The generator's (scale, min) keep every dequantised weight exact in float32."""
-    cfg = synth.config(1)
+    cfg = synth.config("two_slots_mtp")
     codes, meta = synth.qmatrix(np.random.default_rng(3), 1, 32, cfg.hidden, 4)
     q = oracle_lib.qmat(codes[0], meta[0], 32, cfg.hidden, 4)
     W = oracle_lib.dequant(q)
@@ -107,7 +107,7 @@ def test_generated_weights_are_exact_in_float32(oracle_lib):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_router_logits_match_float64_matmul(oracle_lib, dtype):
-    cfg = synth.config(1, x_dtype=dtype)
+    cfg = synth.config("two_slots_mtp", x_dtype=dtype)
     gate_w, _ = synth.make_router(cfg)
     x = synth.make_window(cfg, 5)
     logits, probs, idx, w = oracle_lib.route(x, gate_w, None, cfg.top_k)
@@ -156,7 +156,7 @@ def test_softmax_properties(oracle_lib):
 
 @pytest.mark.parametrize("renorm", [False, True])
 def test_topk_matches_lexsort(oracle_lib, renorm):
-    cfg = synth.config(2)
+    cfg = synth.config("four_slots_mtp_zipf")
     gate_w, bias = synth.make_router(cfg)
     x = synth.make_window(cfg, 1)
     logits, probs, idx, w = oracle_lib.route(x, gate_w, bias, cfg.top_k, renorm)
@@ -184,7 +184,7 @@ def test_topk_forced_ties_take_lower_index(oracle_lib):
 # ------------------------------------------------------------------ grouping
 
 def test_grouping_bruteforce(oracle_lib):
-    cfg = synth.config(2)
+    cfg = synth.config("four_slots_mtp_zipf")
     gate_w, bias = synth.make_router(cfg)
     for win in range(3):
         x = synth.make_window(cfg, win)
@@ -216,7 +216,7 @@ def test_grouping_bruteforce(oracle_lib):
 # ------------------------------------------------------------------ experts
 
 def _single_expert_cfg():
-    return synth.config(0, experts=1, top_k=1)
+    return synth.config("small_f32", experts=1, top_k=1)
 
 
 def test_single_expert_reduces_to_dense_swiglu(oracle_lib):
@@ -258,7 +258,7 @@ def test_zero_up_projection_gives_zero(oracle_lib):
     H, F, bits = 256, 128, 4
     rng = np.random.default_rng(6)
     x = rng.standard_normal(H)
-    cfg = synth.config(0)
+    cfg = synth.config("small_f32")
     g = synth.qmatrix(rng, 1, F, H, bits)
     d = synth.qmatrix(rng, 1, H, F, bits)
     zero_meta = np.zeros(F * H // 32, np.uint32)
@@ -275,9 +275,9 @@ def _layer_qmats(oracle_lib, layer, cfg):
             qm(layer.sh_gate, 1, F, H), qm(layer.sh_up, 1, F, H), qm(layer.sh_down, 1, H, F))
 
 
-@pytest.mark.parametrize("cid,renorm,residual", [(0, False, False), (0, True, True)])
-def test_layer_matches_dense_bruteforce_masked(oracle_lib, cid, renorm, residual):
-    cfg = synth.config(cid)
+@pytest.mark.parametrize("renorm,residual", [(False, False), (True, True)])
+def test_layer_matches_dense_bruteforce_masked(oracle_lib, renorm, residual):
+    cfg = synth.config("small_f32")
     layer = synth.make_layer(cfg)
     mats = _layer_qmats(oracle_lib, layer, cfg)
     for win in range(2):
@@ -290,8 +290,8 @@ def test_layer_matches_dense_bruteforce_masked(oracle_lib, cid, renorm, residual
 
 
 def test_reduced_shape_bf16_pairs_zipf_bruteforce(oracle_lib):
-    """A reduced cid-2-like window: bf16 pairs, Zipf prior, 8 rows, 2-bit weights."""
-    cfg = synth.config(2, hidden=256, ffn=256, experts=12, top_k=3, bits=2)
+    """A reduced four_slots_mtp_zipf-like window: bf16 pairs, Zipf prior, 8 rows, 2-bit weights."""
+    cfg = synth.config("four_slots_mtp_zipf", hidden=256, ffn=256, experts=12, top_k=3, bits=2)
     layer = synth.make_layer(cfg)
     mats = _layer_qmats(oracle_lib, layer, cfg)
     x = synth.make_window(cfg, 3)
@@ -304,7 +304,7 @@ def test_reduced_shape_bf16_pairs_zipf_bruteforce(oracle_lib):
 
 def test_full_mixture_when_k_equals_e(oracle_lib):
     """k = E with renormalisation: the output is the full softmax mixture of all experts."""
-    cfg = synth.config(0, experts=4, top_k=4)
+    cfg = synth.config("small_f32", experts=4, top_k=4)
     layer = synth.make_layer(cfg)
     mats = _layer_qmats(oracle_lib, layer, cfg)
     x = synth.make_window(cfg, 2)
@@ -323,7 +323,7 @@ def test_full_mixture_when_k_equals_e(oracle_lib):
 
 def test_window_row_equals_row_alone(oracle_lib):
     """Batching invariance (Strata docs/BATCHING.md, "Exactness"): bitwise in the oracle."""
-    cfg = synth.config(0, rows=2)
+    cfg = synth.config("small_f32", rows=2)
     layer = synth.make_layer(cfg)
     mats = _layer_qmats(oracle_lib, layer, cfg)
     x = synth.make_window(cfg, 4)
@@ -337,7 +337,7 @@ def test_window_row_equals_row_alone(oracle_lib):
 
 
 def test_x_next_is_bf16_of_output(oracle_lib):
-    cfg = synth.config(1, hidden=256, ffn=128, experts=8, top_k=2)
+    cfg = synth.config("two_slots_mtp", hidden=256, ffn=128, experts=8, top_k=2)
     layer = synth.make_layer(cfg)
     mats = _layer_qmats(oracle_lib, layer, cfg)
     x = synth.make_window(cfg, 0)
@@ -352,7 +352,7 @@ def test_x_next_is_bf16_of_output(oracle_lib):
 # ------------------------------------------------------------------ head
 
 def test_head_matches_dense_and_argmax(oracle_lib):
-    cfg = synth.config(3, vocab=512, hidden=256)
+    cfg = synth.config("stack24_head", vocab=512, hidden=256)
     codes, meta = synth.make_head(cfg)
     q = oracle_lib.qmat(codes[0], meta[0], cfg.vocab, cfg.hidden, 8)
     x = synth.make_window(cfg, 0)
