@@ -85,7 +85,8 @@ def source_sha(files):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = ["verify_window_expert_amd/csrc/moe.hip", "verify_window_expert_amd/csrc/common.h"]
+KERNEL_SOURCES = ["verify_window_expert_amd/csrc/moe.hip", "verify_window_expert_amd/csrc/common.h",
+                  "verify_window_expert_amd/csrc/route_core.h"]
 
 
 def counter_traffic(kernel, workload):
