@@ -54,7 +54,10 @@ def parse():
     p.add_argument("--path", choices=["layer", "split"], default="layer",
                    help="layer: strata_window_layer (router, then gate/up with the routing in every "
                         "workgroup, then down); split: strata_window_route, then strata_window_moe")
-    p.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget (0: skip)")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="oracle sample budget on all host threads (0: skip); a quarter of it more on one thread")
+    p.add_argument("--replays", type=int, default=20,
+                   help="further replays of the timed graph, whose median is reported beside the timed one")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first copy this many MiB device to device three times (a dispatch of known "
                         "bytes for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -71,6 +74,38 @@ def calibration_copy(torch, mib):
     torch.cuda.synchronize()
     log(f"[bench] calibration copy: 3 x {mib} MiB read + {mib} MiB written")
     del src, dst
+
+
+def stream_read_gbs(torch, sw, gib=2, reps=10):
+    """The bandwidth a plain streaming read of HBM reaches on this GPU
+    (strata_window_stream_read over gib GiB, the mean of reps dispatches, each timed by
+    events that the dispatch records)."""
+    src = torch.ones(gib << 28, dtype=torch.int32, device="cuda")   # gib GiB
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        sw.strata_window_stream_read(src, sink)
+    evs = events(torch, 2 * reps)
+    for i in range(reps):
+        sw.strata_window_stream_read(src, sink, prof=[evs[2 * i].cuda_event, evs[2 * i + 1].cuda_event])
+    torch.cuda.synchronize()
+    ms = sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(reps)) / reps
+    nbytes = src.numel() * 4
+    del src, sink
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def replay_median_ms(torch, g, n):
+    """Median duration of n further replays of graph g (each between two events)."""
+    out = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    out.sort()
+    return out[len(out) // 2]
 
 
 def bpw(bits):
@@ -235,11 +270,15 @@ def window_tail_kernels(torch, sw, st, cfg, P):
     return out
 
 
-def cpu_baseline(cfg, host_layer, seconds):
-    """The CPU oracle, as it stands, on windows of the same workload until `seconds` pass."""
+def cpu_baseline(cfg, host_layer, seconds, threads=None):
+    """The CPU oracle, as it stands, on windows of the same workload until `seconds` pass
+    (on `threads` OpenMP threads, else all the host offers)."""
     import oracle
     import synth
     oracle.build(force=False)
+    all_threads = oracle.threads()
+    if threads:
+        oracle.set_threads(threads)
     H, F, E, b = cfg.hidden, cfg.ffn, cfg.experts, cfg.bits
     q = lambda m, n, r, c: oracle.qmat(m[0], m[1], r, c, b, n)
     L = host_layer
@@ -255,9 +294,11 @@ def cpu_baseline(cfg, host_layer, seconds):
         if time.time() - t0 >= seconds:
             break
     dt = time.time() - t0
-    return {"value": round(cfg.rows * n / dt, 3), "unit": "rows/s", "cores": oracle.threads(), "kind": "oracle",
+    used = oracle.threads()
+    oracle.set_threads(all_threads)
+    return {"value": round(cfg.rows * n / dt, 3), "unit": "rows/s", "cores": used, "kind": "oracle",
             "sample": f"{n} windows of this workload (layer instance 0, windows 0..{n - 1}): route, grouping and "
-                      f"experts, {dt:.1f} s wall clock, OpenMP threads = {oracle.threads()}"}
+                      f"experts, {dt:.1f} s wall clock, OpenMP threads = {used}"}
 
 
 def main():
@@ -330,6 +371,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = e0.elapsed_time(e1)
+    ms_med = replay_median_ms(torch, g, args.replays) if args.replays > 0 else None
     U = st.distinct_experts(K)
 
     H, F, E, R = cfg.hidden, cfg.ffn, cfg.experts, cfg.rows
@@ -350,10 +392,15 @@ def main():
             "avg_launch_us": round(1e3 * sum(d_gu) / P, 3),
             "algorithmic_bytes_per_launch": round(sum(gu_bytes) / P)}
 
-    cpu = None
+    del g
+    torch.cuda.synchronize()
+    log("[bench] streaming read of 2 GiB")
+    stream = stream_read_gbs(torch, sw)
+    cpu = cpu1 = None
     if args.cpu_seconds > 0:
-        log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget)")
+        log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget, then a quarter of it on one thread)")
         cpu = cpu_baseline(cfg, st.host_layer0, args.cpu_seconds)
+        cpu1 = cpu_baseline(cfg, st.host_layer0, args.cpu_seconds / 4, threads=1)
 
     workload = {"four_slots_mtp_zipf": "one MoE layer, 8-row verify window (4 slots x token+MTP proposal, Zipf(1.1) router prior, "
                    "correlated pairs), hidden 2048, ffn 768, 128 experts top-8 + shared, 4-bit blocks of 32",
@@ -369,12 +416,15 @@ def main():
                    "top_k": cfg.top_k, "bits": cfg.bits, "layer_instances": args.layers,
                    "windows_in_flight": NF, "path": args.path},
         "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "stream_read_gbs": round(stream, 1), "hbm_frac_of_stream_read": round(gbs / stream, 4),
+        "ms_per_step_median_of_replays": None if ms_med is None else round(ms_med / K, 5),
+        "replays": args.replays,
         "mean_distinct_experts": round(float(U.mean()), 2),
         "unique_weight_bytes_per_window": round(bytes_total / K),
         "kernel_us": dict({"route": round(1e3 * sum(d_route) / P, 3), "gateup": round(1e3 * sum(d_gu) / P, 3),
                            "down": round(1e3 * sum(d_dn) / P, 3)}, **d_post),
         "wall_s": round(wall, 4),
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "cpu_baseline": cpu, "cpu_baseline_1_thread": cpu1,
     }
     print(json.dumps(line), flush=True)
 
@@ -445,6 +495,7 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    ms_med = replay_median_ms(torch, g, min(args.replays, 5)) if args.replays > 0 else None
     U = (n_act - 1).cpu().numpy()
     b_x = 3 * F * H * bpw(cfg.bits)
     b_h = cfg.vocab * H * (1 + 2 / 32)
@@ -457,6 +508,7 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
                                    "residual, then an 8-bit head of vocab 151936 with argmax, 8-row window",
                        "name": "stack24_head", "path": args.path},
             "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "ms_per_step_median_of_replays": None if ms_med is None else round(ms_med / K, 5),
             "kernel_us": {"head": round(head_us, 3)},
             "roofline": {"bound": "hbm", "achieved": round(b_h / (head_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(b_h / (head_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),

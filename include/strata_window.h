@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define STRATA_WINDOW_ABI_VERSION 3
+#define STRATA_WINDOW_ABI_VERSION 4
 
 enum { STRATA_OK = 0, STRATA_EINVAL = -1, STRATA_EUNSUPPORTED = -2, STRATA_EHIP = -3 };
 enum { STRATA_F32 = 0, STRATA_BF16 = 1 };       /* activation dtypes                */
@@ -256,6 +256,21 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
 int strata_window_tier(void* stream, const uint8_t* row_mask, int n_experts, float* counts, float decay,
                        uint8_t* resident, int max_swaps, float min_gain, int32_t* swaps,
                        int32_t* n_swaps, void* const* prof_events);
+
+/*
+ * strata_window_stream_read - a plain streaming read of `bytes` bytes at `src` (16-byte
+ * words, non-temporal, a grid of 8 workgroups per compute unit): the bandwidth that HBM
+ * actually delivers to a read, against which the layer's kernels are compared (the
+ * roofline of the layer is this read of its weights). Measurement only; it computes
+ * nothing of the layer.
+ *   src   device, 16-byte aligned, bytes a nonzero multiple of 16
+ *   sink  device uint32 [1]: written only when the xor of every word equals magic, so
+ *         the caller chooses whether anything is written at all
+ *   prof_events: NULL or {start, end} events recorded by the dispatch.
+ * Errors: STRATA_EINVAL for NULL / misaligned pointers or a bad size.
+ */
+int strata_window_stream_read(void* stream, const void* src, size_t bytes, uint32_t* sink,
+                              uint32_t magic, void* const* prof_events);
 
 /* Workspace bytes for which = 0 (route), 1 (moe), 2 (head), 3 (layer); 0 for invalid
  * arguments. */

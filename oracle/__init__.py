@@ -66,6 +66,7 @@ def lib():
         L.oracle_tier_count.argtypes = [I, P, P, ctypes.c_float]; L.oracle_tier_count.restype = None
         L.oracle_tier_select.argtypes = [I, P, P, I, ctypes.c_float, P]; L.oracle_tier_select.restype = I
         L.oracle_threads.argtypes = []; L.oracle_threads.restype = I
+        L.oracle_set_threads.argtypes = [I]; L.oracle_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -222,3 +223,8 @@ def tier_select(counts, resident, max_swaps, min_gain=1.5):
 
 def threads():
     return lib().oracle_threads()
+
+
+def set_threads(n):
+    """Threads for the oracle's parallel loops from now on."""
+    lib().oracle_set_threads(int(n))

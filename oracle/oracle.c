@@ -416,6 +416,16 @@ int oracle_tier_select(int E, const float* counts, uint8_t* resident, int max_sw
   return n;
 }
 
+/* Threads for the parallel loops above (n >= 1; no effect without OpenMP). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Threads OpenMP would use for the parallel loops above (1 without OpenMP). */
 int oracle_threads(void) {
 #ifdef _OPENMP

@@ -42,7 +42,7 @@ def test_abi_version(sw):
     """The built library reports the version its header declares."""
     text = open(os.path.join(ROOT, "include", "strata_window.h")).read()
     declared = int(re.search(r"#define STRATA_WINDOW_ABI_VERSION (\d+)", text).group(1))
-    assert declared == 3
+    assert declared == 4
     assert sw.library().strata_window_abi_version() == declared
 
 
@@ -219,3 +219,15 @@ def test_layer_rejects_and_workspace(sw):
     assert call(out=A + 4) == sw.STRATA_EINVAL           # moe output
     assert call(F=640) == sw.STRATA_EINVAL               # matrices of another shape
     assert call(ws_bytes=L.strata_window_workspace(1, 8, 2048, 768, 128, 8, 0)) == sw.STRATA_EINVAL
+
+
+def test_stream_read_rejects(sw):
+    L = sw.library()
+    def call(src=A, nbytes=1 << 20, sink=A):
+        return L.strata_window_stream_read(None, src, nbytes, sink, 0x9E3779B9, None)
+    assert call(src=None) == sw.STRATA_EINVAL
+    assert call(src=A + 8) == sw.STRATA_EINVAL
+    assert call(nbytes=0) == sw.STRATA_EINVAL
+    assert call(nbytes=1000) == sw.STRATA_EINVAL
+    assert call(sink=None) == sw.STRATA_EINVAL
+    assert call(sink=A + 2) == sw.STRATA_EINVAL

@@ -63,6 +63,8 @@ def library():
         L.strata_window_accept.restype = I
         L.strata_window_tier.argtypes = [P, P, I, P, ctypes.c_float, P, I, ctypes.c_float, P, P, P]
         L.strata_window_tier.restype = I
+        L.strata_window_stream_read.argtypes = [P, P, S, P, ctypes.c_uint32, P]
+        L.strata_window_stream_read.restype = I
         L.strata_window_workspace.argtypes = [I, I, I, I, I, I, I]
         L.strata_window_workspace.restype = S
         L.strata_window_last_error.argtypes = []
@@ -299,6 +301,15 @@ def strata_window_accept(argmax, proposal=None, mtp=True, tokens=None, n_tokens=
                                           _ptr(proposal) if mtp else None, _ptr(tokens), _ptr(n_tokens),
                                           _ptr(n_accepted), _events(prof)))
     return tokens, n_tokens, n_accepted
+
+
+def strata_window_stream_read(src, sink, magic=0x9E3779B9, stream=None, prof=None):
+    """A plain streaming read of the device tensor src (all its bytes; a nonzero multiple of
+    16): the bandwidth yardstick. sink: a device tensor of at least 4 bytes, written only if
+    the xor of every 16-byte word of src equals magic."""
+    _need(src, "src"); _need(sink, "sink")
+    _check(library().strata_window_stream_read(_stream(stream), _ptr(src), src.numel() * src.element_size(),
+                                               _ptr(sink), int(magic) & 0xFFFFFFFF, _events(prof)))
 
 
 def strata_window_tier(row_mask, counts, decay=1.0, resident=None, max_swaps=0, min_gain=1.5, swaps=None,

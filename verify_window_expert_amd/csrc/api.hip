@@ -357,6 +357,18 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
   return launch_status(sw::launch_accept(a, (hipStream_t)stream, prof_events ? &pa : nullptr), "accept");
 }
 
+int strata_window_stream_read(void* stream, const void* src, size_t bytes, uint32_t* sink, uint32_t magic,
+                              void* const* prof_events) {
+  g_err[0] = 0;
+  if (!src || !aligned(src, 16)) return fail(STRATA_EINVAL, "src NULL or not 16-byte aligned");
+  if (!sink || !aligned(sink, 4)) return fail(STRATA_EINVAL, "sink NULL or not 4-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(STRATA_EINVAL, "bytes %zu not a nonzero multiple of 16", bytes);
+  sw::StreamArgs a;
+  a.src = src; a.words = bytes / 16; a.sink = sink; a.magic = magic;
+  const sw::Prof pa = prof(prof_events, 0);
+  return launch_status(sw::launch_stream_read(a, (hipStream_t)stream, prof_events ? &pa : nullptr), "stream_read");
+}
+
 int strata_window_tier(void* stream, const uint8_t* row_mask, int n_experts, float* counts, float decay,
                        uint8_t* resident, int max_swaps, float min_gain, int32_t* swaps, int32_t* n_swaps,
                        void* const* prof_events) {

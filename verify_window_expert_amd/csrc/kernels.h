@@ -69,6 +69,11 @@ struct TierArgs {
   int32_t* swaps; int32_t* n_swaps;
 };
 
+struct StreamArgs {
+  const void* src; size_t words;   // 16-byte words
+  uint32_t* sink; uint32_t magic;  // written only if the fold of every word equals magic
+};
+
 // Optional timing events of one launch (both may be null): recorded by the dispatch
 // itself at the kernel's start and end (hipExtLaunchKernel).
 struct Prof {
@@ -87,8 +92,8 @@ inline void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, c
 // Launchers return the hipError_t of the launch (0 on success).
 int launch_route(const RouteArgs& a, hipStream_t s, const Prof* p);
 int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
-// the fused layer's gate/up: routing from a.route's partials in every workgroup (workgroup
-// 0 writes the routing outputs), then gate/up as launch_gateup
+// the fused layer's gate/up: routing from a.route's partials in every workgroup (one more
+// workgroup writes the routing outputs), then gate/up as launch_gateup
 int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
 // the router's GEMV alone (the fused layer's first kernel)
 int launch_route_logits(const RouteArgs& a, hipStream_t s, const Prof* p);
@@ -96,6 +101,7 @@ int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
 int launch_tier(const TierArgs& a, hipStream_t s, const Prof* p);
+int launch_stream_read(const StreamArgs& a, hipStream_t s, const Prof* p);
 int head_workgroups(int vocab);
 int down_ranges(int hidden);
 // dynamic LDS of the gate/up and down kernels (the activation image)
