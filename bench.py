@@ -51,9 +51,11 @@ def parse():
     p.add_argument("--inflight", type=int, default=1,
                    help="independent windows in flight (windows alternate over this many streams, "
                         "like pipelined slot groups); 1 = one window after the other")
-    p.add_argument("--path", choices=["layer", "split"], default="layer",
-                   help="layer: strata_window_layer (router, then gate/up with the routing in every "
-                        "workgroup, then down); split: strata_window_route, then strata_window_moe")
+    p.add_argument("--path", choices=["layer", "split", "stack"], default=None,
+                   help="layer (the default for one layer): strata_window_layer (router, then gate/up with "
+                        "the routing in every workgroup, then down); split: strata_window_route, then "
+                        "strata_window_moe; stack (the default for stack24_head): the whole stack and the "
+                        "head in one strata_window_stack call")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="oracle sample budget on all host threads (0: skip); a quarter of it more on one thread")
     p.add_argument("--replays", type=int, default=20,
@@ -143,6 +145,34 @@ def counter_traffic(kernel, workload):
         return None
 
 
+def route_views(sw, torch, n, R, E, k):
+    """n sets of routing outputs, as views into padded device arrays (16-byte aligned
+    slices): (the arrays by name, the n RouteOut views)."""
+    A = min(E, R * k) + 1
+    ent = R * k + R
+    pad = lambda m: (m + 63) // 64 * 64
+    i32, f32 = torch.int32, torch.float32
+    dev = "cuda"
+    big = dict(topk_idx=torch.empty(n, pad(R * k), dtype=i32, device=dev),
+               topk_w=torch.empty(n, pad(R * k), dtype=f32, device=dev),
+               n_active=torch.zeros(n, 64, dtype=i32, device=dev),
+               active=torch.empty(n, pad(A), dtype=i32, device=dev),
+               offsets=torch.empty(n, pad(A + 1), dtype=i32, device=dev),
+               entry_row=torch.empty(n, pad(ent), dtype=i32, device=dev),
+               entry_w=torch.empty(n, pad(ent), dtype=f32, device=dev),
+               row_mask=torch.empty(n, pad(E + 1), dtype=torch.uint8, device=dev),
+               entry_pos=torch.empty(n, pad(ent), dtype=i32, device=dev),
+               row_w=torch.empty(n, pad(R * (k + 1)), dtype=f32, device=dev))
+    views = []
+    for i in range(n):
+        ro = sw.RouteOut.__new__(sw.RouteOut)
+        ro.rows, ro.n_experts, ro.top_k = R, E, k
+        for name, t in big.items():
+            setattr(ro, name, t[i])
+        views.append(ro)
+    return big, views
+
+
 class Steps:
     """Device state of K steps: layers, windows, per-step routing outputs, workspaces."""
 
@@ -161,29 +191,9 @@ class Steps:
                 self.host_layer0 = L
             log(f"[bench] layer {l + 1}/{n_layers} resident ({time.time() - t0:.1f}s)")
         self.xs = [to_dev_x(synth.make_window(cfg, w, rows=R)) for w in range(n_windows)]
-        # per-step routing outputs: views into padded device arrays (16-byte aligned slices)
-        A = min(E, R * k) + 1
-        ent = R * k + R
-        pad = lambda n: (n + 63) // 64 * 64
-        i32, f32 = torch.int32, torch.float32
+        # per-step routing outputs (so the timed graph holds no copies)
         dev = "cuda"
-        self.big = dict(topk_idx=torch.empty(steps, pad(R * k), dtype=i32, device=dev),
-                        topk_w=torch.empty(steps, pad(R * k), dtype=f32, device=dev),
-                        n_active=torch.zeros(steps, 64, dtype=i32, device=dev),
-                        active=torch.empty(steps, pad(A), dtype=i32, device=dev),
-                        offsets=torch.empty(steps, pad(A + 1), dtype=i32, device=dev),
-                        entry_row=torch.empty(steps, pad(ent), dtype=i32, device=dev),
-                        entry_w=torch.empty(steps, pad(ent), dtype=f32, device=dev),
-                        row_mask=torch.empty(steps, pad(E + 1), dtype=torch.uint8, device=dev),
-                        entry_pos=torch.empty(steps, pad(ent), dtype=i32, device=dev),
-                        row_w=torch.empty(steps, pad(R * (k + 1)), dtype=f32, device=dev))
-        self.routes = []
-        for i in range(steps):
-            ro = sw.RouteOut.__new__(sw.RouteOut)
-            ro.rows, ro.n_experts, ro.top_k = R, E, k
-            for name, t in self.big.items():
-                setattr(ro, name, t[i])
-            self.routes.append(ro)
+        self.big, self.routes = route_views(sw, torch, steps, R, E, k)
         # one set of workspaces and outputs per window in flight
         self.ws_r = [sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E)) for _ in range(inflight)]
         self.ws_m = [sw.workspace(sw.workspace_bytes(1 if path == "split" else 3, R, H, cfg.ffn, E, k))
@@ -318,7 +328,12 @@ def main():
         calibration_copy(torch, args.calibrate_copy_mib)
 
     if args.workload == "stack24_head":
+        args.path = args.path or "stack"
         return bench_stack(args, torch, synth, sw, DevLayer, to_dev_x)
+    args.path = args.path or "layer"
+    if args.path == "stack":
+        print(json.dumps({"error": "--path stack is for --workload stack24_head"}))
+        sys.exit(2)
     cfg = synth.config(args.workload, **({"rows": args.rows} if args.rows else {}))
     K, W = args.steps, args.warmup
     NF = max(1, args.inflight)
@@ -442,7 +457,9 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
     codes, meta = synth.make_head(cfg)
     head = sw.upload_qmat(codes, meta, cfg.vocab, H, 8)
     xs = [to_dev_x(synth.make_window(cfg, w)) for w in range(16)]
-    routes = [sw.RouteOut(R, E, k) for _ in range(cfg.layers)]
+    # per-step, per-layer routing outputs: the timed graph holds the stack's kernels only
+    big, rviews = route_views(sw, torch, K * cfg.layers, R, E, k)
+    routes_of = lambda i: rviews[(i % K) * cfg.layers:(i % K + 1) * cfg.layers]
     ws_r = sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E))
     ws_m = sw.workspace(sw.workspace_bytes(1 if args.path == "split" else 3, R, H, F, E, k))
     ws_h = sw.workspace(sw.workspace_bytes(2, R, H, vocab=cfg.vocab))
@@ -451,32 +468,38 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
     out = torch.empty(R, H, dtype=torch.float32, device="cuda")
     logits = torch.empty(R, cfg.vocab, dtype=torch.float32, device="cuda")
     am = torch.empty(8, dtype=torch.int32, device="cuda")
-    n_act = torch.zeros(K, cfg.layers, dtype=torch.int32, device="cuda")
+    stack_layers = [(dl.gate_w, dl.bias, dl.gate, dl.up, dl.down, *dl.sh) for dl in layers]
+    ws_s = sw.workspace(sw.workspace_bytes(4, R, H, F, E, k, cfg.vocab)) if args.path == "stack" else None
 
-    def step(i, record=True, prof_head=None):
-        xa.copy_(xs[i % len(xs)])
-        cur, nxt = xa, xb
+    def step(i, prof_head=None):
+        x0, routes = xs[i % len(xs)], routes_of(i)
+        if args.path == "stack":
+            sw.strata_window_stack(x0, stack_layers, k, head=head, routes=routes, logits=logits, argmax=am, out=out,
+                                   x_final=xb, ws=ws_s)
+            if prof_head is not None:   # the head's own duration: the same head once more, timed
+                sw.strata_window_head(xb, head, logits=logits, argmax=am, ws=ws_h, prof=prof_head)
+            return
+        # layer 0 reads the window itself; the later inputs alternate between xa and xb
+        cur, nxt = x0, xa
         for l, dl in enumerate(layers):
             if args.path == "layer":
-                _, ro = sw.strata_window_layer(cur, dl.gate_w, dl.bias, k, dl.gate, dl.up, dl.down, *dl.sh,
-                                               route=routes[l], residual=cur, out=out, x_next=nxt, ws=ws_m)
+                sw.strata_window_layer(cur, dl.gate_w, dl.bias, k, dl.gate, dl.up, dl.down, *dl.sh,
+                                       route=routes[l], residual=cur, out=out, x_next=nxt, ws=ws_m)
             else:
                 ro = sw.strata_window_route(cur, dl.gate_w, dl.bias, k, out=routes[l], ws=ws_r)
                 sw.strata_window_moe(cur, dl.gate, dl.up, dl.down, *dl.sh, ro, residual=cur, out=out, x_next=nxt,
                                      ws=ws_m)
-            if record:
-                n_act[i, l].copy_(ro.n_active[0])
-            cur, nxt = nxt, cur
+            cur, nxt = nxt, (xb if nxt is xa else xa)
         sw.strata_window_head(cur, head, logits=logits, argmax=am, ws=ws_h, prof=prof_head)
 
     for i in range(W):
-        step(i, record=False)
+        step(i)
     torch.cuda.synchronize()
     # the head's duration: events recorded by its own dispatches, over eager steps
     P = 16
     hev = events(torch, 2 * P)
     for i in range(P):
-        step(i, record=False, prof_head=[hev[2 * i].cuda_event, hev[2 * i + 1].cuda_event])
+        step(i, prof_head=[hev[2 * i].cuda_event, hev[2 * i + 1].cuda_event])
     torch.cuda.synchronize()
     head_us = 1e3 * sum(hev[2 * i].elapsed_time(hev[2 * i + 1]) for i in range(P)) / P
     g = torch.cuda.CUDAGraph()
@@ -496,7 +519,8 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     ms_med = replay_median_ms(torch, g, min(args.replays, 5)) if args.replays > 0 else None
-    U = (n_act - 1).cpu().numpy()
+    # every step's routing, as the replays wrote it: [step][layer] distinct routed experts
+    U = (big["n_active"][:K * cfg.layers, 0].view(K, cfg.layers) - 1).cpu().numpy()
     b_x = 3 * F * H * bpw(cfg.bits)
     b_h = cfg.vocab * H * (1 + 2 / 32)
     bytes_total = float((4 * E * H + (U + 1) * b_x).sum() + K * b_h)

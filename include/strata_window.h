@@ -31,7 +31,8 @@
  *     durations: route {start of its first kernel, end of its last}; moe {gate/up
  *     start, gate/up end, down start, end of the combine}; layer {router GEMV start, end,
  *     gate/up (with the routing) start, end, down start, end of the combine}; head
- *     {start, end}; accept and tier {start, end}. A NULL
+ *     {start, end}; accept, tier and stream_read {start, end}; stack {start of its first
+ *     kernel, end of its last}. A NULL
  *     entry is skipped. Pass NULL while the stream is being captured into a graph.
  *   - Workspace `ws`: at least strata_window_workspace(...) bytes of scratch (partial
  *     sums and intermediates; the first STRATA_WS_COUNTER_BYTES bytes are reserved).
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define STRATA_WINDOW_ABI_VERSION 4
+#define STRATA_WINDOW_ABI_VERSION 5
 
 enum { STRATA_OK = 0, STRATA_EINVAL = -1, STRATA_EUNSUPPORTED = -2, STRATA_EHIP = -3 };
 enum { STRATA_F32 = 0, STRATA_BF16 = 1 };       /* activation dtypes                */
@@ -58,6 +59,7 @@ enum { STRATA_ROUTE_RENORM = 1 };                /* route flag: divide top-k wei
                                                     by their sum                     */
 enum { STRATA_MAX_ROWS = 8, STRATA_MAX_TOPK = 8, STRATA_MAX_EXPERTS = 256 };
 enum { STRATA_MAX_FFN = 4096 };                  /* strata_window_moe: widest ffn    */
+enum { STRATA_MAX_LAYERS = 1024 };               /* strata_window_stack              */
 #define STRATA_WS_COUNTER_BYTES 4096
 
 /*
@@ -272,8 +274,52 @@ int strata_window_tier(void* stream, const uint8_t* row_mask, int n_experts, flo
 int strata_window_stream_read(void* stream, const void* src, size_t bytes, uint32_t* sink,
                               uint32_t magic, void* const* prof_events);
 
-/* Workspace bytes for which = 0 (route), 1 (moe), 2 (head), 3 (layer); 0 for invalid
- * arguments. */
+/*
+ * strata_layer - one MoE layer of a stack (host struct, read during the call): its
+ * router (gate_w [n_experts][hidden] float, logit_bias [n_experts] float or NULL), its six
+ * matrix families as in strata_window_moe, and where its window's routing is written
+ * (strata_route_out; layers may share one, since each layer's routing is used before
+ * the next layer's is written).
+ */
+typedef struct {
+  const float* gate_w;
+  const float* logit_bias;
+  strata_qmat gate, up, down, sh_gate, sh_up, sh_down;
+  strata_route_out route;
+} strata_layer;
+
+/*
+ * strata_window_stack - one window through a stack of n_layers MoE layers and then,
+ * optionally, the 8-bit head: a pipeline stage's share of the model for one window
+ * (Strata docs/MULTI_GPU.md, "What each card holds": a card holds a contiguous range of
+ * layers, the last one also the head; PR #1636, "What changed": every stage runs the
+ * eight-row verify windows). Layer l computes what strata_window_layer computes with
+ * residual = its input x_l, and x_{l+1} = bf16(x_l + out_l) is the next layer's input
+ * (x_0 = x, in x_dtype; every later x_l is bf16). The call runs three kernels per layer
+ * instead of four: layer l's combine and layer l + 1's router GEMV share one launch, each
+ * of its workgroups forming its own 512-input chunk of x_{l+1} before its share of the
+ * GEMV. Every layer's routing and x_{l+1} equal those of the same layers run one
+ * strata_window_layer call at a time, bit for bit.
+ *   layers   host array [n_layers]; every layer has the shapes hidden, ffn, n_experts,
+ *            top_k and the same bits
+ *   flags    STRATA_ROUTE_RENORM or 0, for every layer
+ *   head     NULL, or the 8-bit head [vocab][hidden] (then argmax [rows] int32 is
+ *            required and logits [rows][vocab] float is optional, as strata_window_head)
+ *   out      NULL or [rows][hidden] float: the last layer's output (residual included)
+ *   x_final  [rows][hidden] bf16: the last layer's x_next, the head's input
+ *   ws: at least strata_window_workspace(4, ..., vocab) bytes (vocab 0 without a head).
+ *   prof_events: NULL or {start of the first kernel, end of the last}.
+ * Errors: those of strata_window_layer for any layer and of strata_window_head; n_layers
+ * outside 1..STRATA_MAX_LAYERS, layers or x_final NULL, or a layer whose bits differ.
+ */
+int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
+                        int n_experts, int top_k, int flags, int n_layers, const strata_layer* layers,
+                        const strata_qmat* head, int vocab, float* logits, int32_t* argmax,
+                        float* out, uint16_t* x_final, void* ws, size_t ws_bytes,
+                        void* const* prof_events);
+
+/* Workspace bytes for which = 0 (route), 1 (moe), 2 (head), 3 (layer), 4 (stack; vocab 0
+ * without a head); 0 for invalid arguments. */
 size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts,
                                int top_k, int vocab);
 

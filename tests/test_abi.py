@@ -42,7 +42,7 @@ def test_abi_version(sw):
     """The built library reports the version its header declares."""
     text = open(os.path.join(ROOT, "include", "strata_window.h")).read()
     declared = int(re.search(r"#define STRATA_WINDOW_ABI_VERSION (\d+)", text).group(1))
-    assert declared == 4
+    assert declared == 5
     assert sw.library().strata_window_abi_version() == declared
 
 
@@ -231,3 +231,28 @@ def test_stream_read_rejects(sw):
     assert call(nbytes=1000) == sw.STRATA_EINVAL
     assert call(sink=None) == sw.STRATA_EINVAL
     assert call(sink=A + 2) == sw.STRATA_EINVAL
+
+
+def test_stack_rejects_and_workspace(sw):
+    L = sw.library()
+    layers = (sw.CLayer * 2)()
+    def call(n=2, lay=layers, xf=A, ws=A, wsb=1 << 30, rows=8, out=None):
+        return L.strata_window_stack(None, A, sw.STRATA_BF16, rows, 2048, 768, 128, 8, 0, n, lay, None, 0, None,
+                                     None, out, xf, ws, wsb, None)
+    assert call(n=0) == sw.STRATA_EINVAL
+    assert call(n=1025) == sw.STRATA_EINVAL
+    assert call(lay=None) == sw.STRATA_EINVAL
+    assert call(xf=None) == sw.STRATA_EINVAL
+    assert call(xf=A + 8) == sw.STRATA_EINVAL
+    assert call(out=A + 4) == sw.STRATA_EINVAL
+    assert call(ws=A + 16) == sw.STRATA_EINVAL
+    assert call(wsb=1024) == sw.STRATA_EINVAL
+    assert call(rows=9) == sw.STRATA_EINVAL
+    assert call() == sw.STRATA_EINVAL            # the layers' descriptors are empty
+    assert "layer 0" in L.strata_window_last_error().decode()
+    # the stack's workspace holds a layer's, two bf16 inputs and the head's
+    w3 = sw.workspace_bytes(3, 8, 2048, 768, 128, 8)
+    w4 = sw.workspace_bytes(4, 8, 2048, 768, 128, 8, 0)
+    w4h = sw.workspace_bytes(4, 8, 2048, 768, 128, 8, 151936)
+    assert w4 >= w3 + 2 * 2 * 8 * 2048
+    assert w4h >= w4 + sw.workspace_bytes(2, 8, 2048, vocab=151936) - 4096

@@ -38,6 +38,11 @@ class CRouteOut(ctypes.Structure):
                  "entry_pos", "row_w")]
 
 
+class CLayer(ctypes.Structure):
+    _fields_ = [("gate_w", ctypes.c_void_p), ("logit_bias", ctypes.c_void_p)] + \
+        [(n, CQMat) for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")] + [("route", CRouteOut)]
+
+
 _lib = None
 
 
@@ -63,6 +68,9 @@ def library():
         L.strata_window_accept.restype = I
         L.strata_window_tier.argtypes = [P, P, I, P, ctypes.c_float, P, I, ctypes.c_float, P, P, P]
         L.strata_window_tier.restype = I
+        L.strata_window_stack.argtypes = [P, P, I, I, I, I, I, I, I, I, ctypes.POINTER(CLayer),
+                                          ctypes.POINTER(CQMat), I, P, P, P, P, P, S, P]
+        L.strata_window_stack.restype = I
         L.strata_window_stream_read.argtypes = [P, P, S, P, ctypes.c_uint32, P]
         L.strata_window_stream_read.restype = I
         L.strata_window_workspace.argtypes = [I, I, I, I, I, I, I]
@@ -260,6 +268,52 @@ def strata_window_layer(x, gate_w, bias, top_k, gate, up, down, sh_gate, sh_up, 
                                          _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws), ws.numel(),
                                          _events(prof)))
     return out, route
+
+
+def strata_window_stack(x, layers, top_k, head=None, renorm=False, routes=None, logits=True, argmax=None,
+                        out=None, x_final=None, ws=None, stream=None, prof=None):
+    """One window through a stack of MoE layers (residual between layers) and, with head,
+    the 8-bit head (see strata_window_stack). layers: a sequence of
+    (gate_w, bias or None, gate, up, down, sh_gate, sh_up, sh_down) with QMat matrices;
+    routes: None (one RouteOut shared by all layers) or one RouteOut per layer.
+    Returns (x_final bf16 [rows, hidden], the routes list, logits or None, argmax or None);
+    out (the last layer's float output) is filled if given."""
+    _need(x, "x")
+    rows, hidden = x.shape
+    n = len(layers)
+    E = layers[0][0].shape[0]
+    ffn = layers[0][2].rows
+    if routes is None:
+        shared = RouteOut(rows, E, top_k, x.device)
+        routes = [shared] * n
+    if len(routes) != n:
+        raise ValueError("one RouteOut per layer, or None")
+    cl = (CLayer * n)()
+    for i, (gw, bias, *mats) in enumerate(layers):
+        _need(gw, "gate_w")
+        if bias is not None:
+            _need(bias, "bias")
+        cl[i] = CLayer(gw.data_ptr(), None if bias is None else bias.data_ptr(), *[q.c() for q in mats],
+                       routes[i].c())
+    if x_final is None:
+        x_final = torch.empty(rows, hidden, dtype=torch.bfloat16, device=x.device)
+    _need(x_final, "x_final")
+    lg = am = None
+    V = 0
+    if head is not None:
+        V = head.rows
+        lg = torch.empty(rows, V, dtype=torch.float32, device=x.device) if logits is True else logits
+        if lg is False:
+            lg = None
+        am = torch.empty(max(rows, 4), dtype=torch.int32, device=x.device) if argmax is None else argmax
+    if ws is None:
+        ws = workspace(workspace_bytes(4, rows, hidden, ffn, E, top_k, V), x.device)
+    hq = head.c() if head is not None else None
+    _check(library().strata_window_stack(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ffn, E, top_k,
+                                         STRATA_ROUTE_RENORM if renorm else 0, n, cl,
+                                         None if hq is None else ctypes.byref(hq), V, _ptr(lg), _ptr(am),
+                                         _ptr(out), _ptr(x_final), _ptr(ws), ws.numel(), _events(prof)))
+    return x_final, routes, lg, (None if am is None else am[:rows])
 
 
 def strata_window_head(x, head, logits=True, argmax=None, ws=None, stream=None, prof=None):

@@ -67,6 +67,20 @@ HeadWs head_ws(int rows, int vocab) {
   return w;
 }
 
+// the stack: one layer's workspace (reused by every layer), the two bf16 inputs of the
+// layers after the first (ping-pong), and the head's
+struct StackWs { LayerWs layer; size_t xa, xb, head; HeadWs hw; size_t total; };
+StackWs stack_ws(int rows, int hidden, int ffn, int E, int top_k, int vocab) {
+  StackWs w;
+  w.layer = layer_ws(rows, hidden, ffn, E, top_k);
+  w.xa = w.layer.total;
+  w.xb = round_up(w.xa + 2 * (size_t)rows * hidden, 256);
+  w.head = round_up(w.xb + 2 * (size_t)rows * hidden, 256);
+  w.hw = head_ws(rows, vocab > 0 ? vocab : 1);
+  w.total = vocab > 0 ? w.head + w.hw.total : w.head;
+  return w;
+}
+
 // ------------------------------------------------------------------------ checks
 
 int check_common(const void* x, int x_dtype, int rows, int hidden, void* ws) {
@@ -161,6 +175,10 @@ size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_e
     case 1: return (ffn >= 1 && top_k >= 1) ? moe_ws(rows, hidden, ffn, top_k).total : 0;
     case 2: return vocab >= 1 ? head_ws(rows, vocab).total : 0;
     case 3: return (ffn >= 1 && top_k >= 1 && n_experts >= 1) ? layer_ws(rows, hidden, ffn, n_experts, top_k).total : 0;
+    case 4:
+      return (ffn >= 1 && top_k >= 1 && n_experts >= 1 && vocab >= 0)
+                 ? stack_ws(rows, hidden, ffn, n_experts, top_k, vocab).total
+                 : 0;
     default: return 0;
   }
 }
@@ -196,7 +214,7 @@ int prepare_moe(const void* x, int x_dtype, int rows, int hidden, int ffn, const
                 const strata_qmat* up, const strata_qmat* down, const strata_qmat* sh_gate, const strata_qmat* sh_up,
                 const strata_qmat* sh_down, const strata_route_out* route, int n_experts, int top_k,
                 const void* residual, float* out, uint16_t* x_next_bf16, void* ws, const MoeWs& w,
-                sw::GateUpArgs& g, sw::DownArgs& d, int& max_slots) {
+                sw::GateUpArgs& g, sw::DownArgs& d, int& max_slots, bool out_optional = false) {
   int rc;
   if ((rc = check_common(x, x_dtype, rows, hidden, ws))) return rc;
   if ((rc = check_experts(n_experts, top_k))) return rc;
@@ -212,7 +230,8 @@ int prepare_moe(const void* x, int x_dtype, int rows, int hidden, int ffn, const
   if ((rc = check_qmat(sh_gate, "sh_gate", ffn, hidden, 1, bits))) return rc;
   if ((rc = check_qmat(sh_up, "sh_up", ffn, hidden, 1, bits))) return rc;
   if ((rc = check_qmat(sh_down, "sh_down", hidden, ffn, 1, bits))) return rc;
-  if (!out || !aligned(out, 16)) return fail(STRATA_EINVAL, "out NULL or not 16-byte aligned");
+  if ((!out && !out_optional) || (out && !aligned(out, 16)))
+    return fail(STRATA_EINVAL, "out NULL or not 16-byte aligned");
   if (residual && !aligned(residual, 16)) return fail(STRATA_EINVAL, "residual not 16-byte aligned");
   if (x_next_bf16 && !aligned(x_next_bf16, 16)) return fail(STRATA_EINVAL, "x_next not 16-byte aligned");
   const size_t lds_gu = sw::gateup_lds_bytes(hidden, x_dtype), lds_dn = sw::down_lds_bytes(ffn);
@@ -309,6 +328,105 @@ int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int 
   if ((rc = launch_status(sw::launch_gateup_routed(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up")))
     return rc;
   return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
+}
+
+int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn, int n_experts,
+                        int top_k, int flags, int n_layers, const strata_layer* layers, const strata_qmat* head,
+                        int vocab, float* logits, int32_t* argmax, float* out, uint16_t* x_final, void* ws,
+                        size_t ws_bytes, void* const* prof_events) {
+  g_err[0] = 0;
+  if (n_layers < 1 || n_layers > STRATA_MAX_LAYERS)
+    return fail(STRATA_EINVAL, "n_layers %d outside 1..%d", n_layers, (int)STRATA_MAX_LAYERS);
+  if (!layers) return fail(STRATA_EINVAL, "layers is NULL");
+  if (!x_final || !aligned(x_final, 16)) return fail(STRATA_EINVAL, "x_final NULL or not 16-byte aligned");
+  if (out && !aligned(out, 16)) return fail(STRATA_EINVAL, "out not 16-byte aligned");
+  if (!ws || !aligned(ws, 256)) return fail(STRATA_EINVAL, "ws NULL or not 256-byte aligned");
+  if (rows < 1 || rows > STRATA_MAX_ROWS || hidden < 1 || ffn < 1 || n_experts < 1 || top_k < 1)
+    return fail(STRATA_EINVAL, "rows %d / hidden %d / ffn %d / n_experts %d / top_k %d out of range", rows, hidden,
+                ffn, n_experts, top_k);
+  const StackWs w = stack_ws(rows, hidden, ffn, n_experts, top_k, head ? vocab : 0);
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "stack workspace %zu < %zu bytes", ws_bytes, w.total);
+  char* const wb = (char*)ws;
+  uint16_t* const xpp[2] = {(uint16_t*)(wb + w.xa), (uint16_t*)(wb + w.xb)};
+  // layer l reads x_l and writes x_{l+1}: x_0 = x; the last layer writes x_final, every
+  // other one the ping-pong buffer that its input is not in
+  auto input = [&](int l) -> const void* { return l == 0 ? x : (const void*)xpp[(l - 1) % 2]; };
+  auto input_dtype = [&](int l) { return l == 0 ? x_dtype : (int)STRATA_BF16; };
+  auto output = [&](int l) { return l == n_layers - 1 ? x_final : xpp[l % 2]; };
+
+  // every check first (nothing is enqueued on an error), then the launches
+  sw::RouteArgs r;
+  sw::GateUpArgs g;
+  sw::DownArgs d;
+  int max_slots = 0, rc;
+  for (int l = 0; l < n_layers; l++) {
+    const strata_layer& L = layers[l];
+    if (L.gate.bits != layers[0].gate.bits)
+      return fail(STRATA_EINVAL, "layer %d: bits %d differ from layer 0's %d", l, L.gate.bits, layers[0].gate.bits);
+    if ((rc = prepare_route(input(l), input_dtype(l), rows, hidden, L.gate_w, L.logit_bias, n_experts, top_k, flags,
+                            &L.route, ws, w.layer.partials, r)) ||
+        (rc = prepare_moe(input(l), input_dtype(l), rows, hidden, ffn, &L.gate, &L.up, &L.down, &L.sh_gate, &L.sh_up,
+                          &L.sh_down, &L.route, n_experts, top_k, input(l), l == n_layers - 1 ? out : nullptr,
+                          output(l), ws, w.layer.moe, g, d, max_slots, true))) {
+      char msg[sizeof g_err];
+      snprintf(msg, sizeof msg, "%s", g_err);
+      return fail(rc, "layer %d: %s", l, msg);
+    }
+    if (sw::gateup_lds_bytes(hidden, input_dtype(l)) + kStaticLds + sw::route_core_lds_bytes() > kLdsLimit)
+      return fail(STRATA_EUNSUPPORTED, "hidden %d: the activations and the routing tables need more than %zu bytes "
+                  "of LDS", hidden, kLdsLimit);
+  }
+  sw::HeadArgs ha;
+  if (head) {
+    if (vocab < 1) return fail(STRATA_EINVAL, "vocab %d < 1", vocab);
+    if ((rc = check_qmat(head, "head", vocab, hidden, 1, 8))) return rc;
+    if (!argmax || !aligned(argmax, 16)) return fail(STRATA_EINVAL, "argmax NULL or not 16-byte aligned");
+    if (logits && !aligned(logits, 16)) return fail(STRATA_EINVAL, "logits not 16-byte aligned");
+    const size_t lds = (size_t)8 * (hidden + 8) * 2 + (size_t)(hidden / 32) * 64;
+    if (lds > kLdsLimit) return fail(STRATA_EUNSUPPORTED, "hidden %d needs more than %zu bytes of LDS", hidden, kLdsLimit);
+    ha.x = x_final; ha.x_dtype = STRATA_BF16; ha.rows = rows; ha.hidden = hidden; ha.vocab = vocab;
+    ha.codes = (const uint8_t*)head->codes; ha.meta = (const uint8_t*)head->meta;
+    ha.logits = logits; ha.argmax = argmax;
+    ha.part_val = (float*)(wb + w.head + w.hw.val); ha.part_idx = (int32_t*)(wb + w.head + w.hw.idx);
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  // the events: the first launch (layer 0's router) records the start, the last (the
+  // head's, else the last layer's combine) the end
+  sw::Prof first, last;
+  if (prof_events) { first.start = (hipEvent_t)prof_events[0]; last.stop = (hipEvent_t)prof_events[1]; }
+  const sw::Prof* p_first = prof_events ? &first : nullptr;
+  const sw::Prof* p_last = prof_events ? &last : nullptr;
+  for (int l = 0; l < n_layers; l++) {
+    const strata_layer& L = layers[l];
+    prepare_route(input(l), input_dtype(l), rows, hidden, L.gate_w, L.logit_bias, n_experts, top_k, flags, &L.route,
+                  ws, w.layer.partials, r);
+    prepare_moe(input(l), input_dtype(l), rows, hidden, ffn, &L.gate, &L.up, &L.down, &L.sh_gate, &L.sh_up,
+                &L.sh_down, &L.route, n_experts, top_k, input(l), l == n_layers - 1 ? out : nullptr, output(l), ws,
+                w.layer.moe, g, d, max_slots, true);
+    g.route = r;
+    const bool last_layer = l == n_layers - 1;
+    if (l == 0 && (rc = launch_status(sw::launch_route_logits(r, s, p_first), "router"))) return rc;
+    if ((rc = launch_status(sw::launch_gateup_routed(g, max_slots, s, nullptr), "gate/up"))) return rc;
+    if ((rc = launch_status(sw::launch_down(d, max_slots, s, last_layer && !head ? p_last : nullptr, last_layer),
+                            "down")))
+      return rc;
+    if (!last_layer) {
+      // layer l's combine and layer l + 1's router in one launch
+      const strata_layer& N = layers[l + 1];
+      sw::RouteArgs rn;
+      prepare_route(output(l), STRATA_BF16, rows, hidden, N.gate_w, N.logit_bias, n_experts, top_k, flags, &N.route,
+                    ws, w.layer.partials, rn);
+      sw::CombineRouteArgs c;
+      c.route = rn;
+      c.y = d.y; c.row_w = d.row_w; c.top_k = top_k;
+      c.x_res = input(l); c.x_next = output(l); c.out = nullptr;
+      if ((rc = launch_status(sw::launch_combine_route(c, input_dtype(l) == STRATA_F32, s, nullptr), "combine + router")))
+        return rc;
+    }
+  }
+  if (head) return launch_status(sw::launch_head(ha, s, p_last), "head");
+  return STRATA_OK;
 }
 
 int strata_window_head(void* stream, const void* x, int x_dtype, int rows, int hidden, const strata_qmat* head,

@@ -14,6 +14,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxRows = 8;
+constexpr int kMaxTopk = 8;
 constexpr int kCounterBytes = 4096;
 
 // ---------------------------------------------------------------- number formats
@@ -35,6 +36,20 @@ __device__ __forceinline__ float f16_lo(uint32_t m) {
 }
 __device__ __forceinline__ float f16_hi(uint32_t m) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
+}
+
+// One output of the combine: the row's k + 1 expert outputs y[j] times their weights w[j]
+// (routed experts in ascending id order, the shared expert last with weight 1), added by
+// fused multiply-adds from zero in that order, then the residual. Every kernel that
+// forms a layer output uses this one definition, so their outputs agree bit for bit.
+__device__ __forceinline__ float combine_one(const float (&w)[kMaxTopk + 1], const float (&y)[kMaxTopk + 1], int k1,
+                                             bool has_res, float res) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j <= kMaxTopk; j++)
+    if (j < k1) s = fmaf(w[j], y[j], s);
+  if (has_res) s += res;
+  return s;
 }
 
 // Activation element i as float. The dtype is a template parameter: a runtime branch

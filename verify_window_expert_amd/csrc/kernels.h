@@ -42,7 +42,7 @@ struct DownArgs {
   const int32_t* entry_pos; const float* row_w;
   const uint32_t* h_img;    // as GateUpArgs
   float* y;                 // [rows][top_k + 1][hidden]: row r's experts in ascending id order
-  float* out; uint16_t* x_next;
+  float* out; uint16_t* x_next;   // out may be NULL (a stack layer whose float output nobody reads)
   int n_ranges;             // 64-row output ranges
   int max_slots, top_k;     // capacity of the active / offsets arrays; routing top-k
 };
@@ -67,6 +67,16 @@ struct TierArgs {
   uint8_t* resident;        // NULL: counting only
   int max_swaps; float min_gain;
   int32_t* swaps; int32_t* n_swaps;
+};
+
+// A stack's hand-over between layers l and l + 1 (one launch): layer l's combine and
+// layer l + 1's router GEMV.
+struct CombineRouteArgs {
+  RouteArgs route;          // layer l + 1's router (its x is formed here, not read)
+  const float* y; const float* row_w; int top_k;   // layer l's expert outputs, weights
+  const void* x_res;        // layer l's input (the residual); nullable
+  uint16_t* x_next;         // [rows][hidden] bf16: layer l + 1's input (written)
+  float* out;               // [rows][hidden] float, nullable: layer l's output
 };
 
 struct StreamArgs {
@@ -97,7 +107,10 @@ int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof*
 int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
 // the router's GEMV alone (the fused layer's first kernel)
 int launch_route_logits(const RouteArgs& a, hipStream_t s, const Prof* p);
-int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p);
+// down, then (combine) the combine kernel
+int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p, bool combine = true);
+// layer l's combine and layer l + 1's router GEMV in one launch (res_f32: layer l's input is float)
+int launch_combine_route(const CombineRouteArgs& c, int res_f32, hipStream_t s, const Prof* p);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
 int launch_tier(const TierArgs& a, hipStream_t s, const Prof* p);

@@ -28,7 +28,6 @@
 namespace sw {
 
 constexpr int kThreads = 256;   // 4 waves
-constexpr int kMaxTopk = 8;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxSlots = kMaxRows * kMaxTopk + 1;   // routed experts a window can use + shared
 #ifndef SW_GU_DEPTH
@@ -776,14 +775,12 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DownArgs a) {
   f32x2 o;
 #pragma unroll
   for (int i = 0; i < 2; i++) {
-    float s = 0.f;
+    float yi[kMaxTopk + 1];
 #pragma unroll
-    for (int j = 0; j <= kMaxTopk; j++)
-      if (j < K1) s = fmaf(w[j], yv[j][i], s);
-    if (a.x_res) s += res[i];
-    o[i] = s;
+    for (int j = 0; j <= kMaxTopk; j++) yi[j] = yv[j][i];
+    o[i] = combine_one(w, yi, K1, a.x_res != nullptr, res[i]);
   }
-  *(f32x2*)(a.out + (long)r * H + n) = o;
+  if (a.out) *(f32x2*)(a.out + (long)r * H + n) = o;
   if (a.x_next)
     *(uint32_t*)(a.x_next + (long)r * H + n) = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
 }
@@ -904,13 +901,14 @@ static int launch_down_bits(const DownArgs& a, size_t lds, int max_slots, hipStr
   return (int)hipErrorInvalidValue;
 }
 
-int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p) {
+int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p, bool combine) {
   const size_t lds = down_lds_bytes(a.ffn);
   Prof p0, p1;
   if (p) { p0.start = p->start; p1.stop = p->stop; }
+  if (!combine) p0.stop = p1.stop;
   const int e = a.bits == 4 ? launch_down_bits<4>(a, lds, max_slots, s, p ? &p0 : nullptr)
                             : launch_down_bits<2>(a, lds, max_slots, s, p ? &p0 : nullptr);
-  if (e) return e;
+  if (e || !combine) return e;
   const int cg = (a.rows * (a.hidden / kCombineVec) + kCombineThreads - 1) / kCombineThreads;
   if (a.x_dtype == 0)
     launch(k_combine<true>, dim3(cg), dim3(kCombineThreads), 0, s, p ? &p1 : nullptr, a);
