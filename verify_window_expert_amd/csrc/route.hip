@@ -5,8 +5,8 @@
 // the router and every routed expert the window's rows use are read once for all of
 // them; the row lists built here are what lets the expert kernels do that.
 //
-// Two launches. k_route_logits: workgroup (expert group eg, input chunk hc), each of its
-// 4 waves owns one expert and 512 inputs and writes one double partial per row.
+// Two launches. k_route_logits: workgroup (row group, expert group, input chunk), each of
+// its 4 waves owns one expert and 512 inputs and writes one double partial per row.
 // k_route_final (one workgroup) adds the partials in chunk order, then runs softmax,
 // top-k and grouping for the whole window. (A completion ticket in one launch would
 // serialise one device-scope atomic per workgroup, which costs more than the launch.)
@@ -65,53 +65,6 @@ __device__ __forceinline__ void route_gemv(const RouteArgs& a, const double (&xs
   }
 }
 
-template <bool F32IN>
-__global__ __launch_bounds__(kRouteThreads) void k_route_logits(RouteArgs a) {
-  __shared__ __align__(16) double xs[kMaxRows][kRouteChunk];
-
-  const int H = a.hidden, R = a.rows;
-  const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
-  const int hc = blockIdx.x % n_hc, eg = blockIdx.x / n_hc;
-  const int h0 = hc * kRouteChunk;
-  const int hn = min(kRouteChunk, H - h0);   // a multiple of 32 (hidden % 32 == 0)
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int e = eg * kRouteWaves + wave;
-
-  float2 gv[kRouteNU];
-  gate_chunk_load(a, e, h0, hn, lane, gv);
-  // the chunk of the window's rows, as doubles (exact): thread t converts row t / 32,
-  // inputs 16 (t % 32) .. +15; rows past R and inputs past hn become 0
-  {
-    const int xr = tid >> 5, xc = 16 * (tid & 31);
-    const bool ok = xr < R && xc < hn;
-    const long base = (long)min(xr, R - 1) * H + h0 + min(xc, hn - 16);
-    float v[16];
-    if constexpr (F32IN) {
-      const u32x4* p = (const u32x4*)((const float*)a.x + base);
-      u32x4 w[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) w[i] = p[i];
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const uint32_t b = w[i >> 2][i & 3];
-        v[i] = __uint_as_float(b);
-      }
-    } else {
-      const u32x4* p = (const u32x4*)((const uint16_t*)a.x + base);
-      u32x4 w[2];
-#pragma unroll
-      for (int i = 0; i < 2; i++) w[i] = p[i];
-#pragma unroll
-      for (int i = 0; i < 16; i++) v[i] = bf16_to_f32((uint16_t)(w[i >> 3][(i >> 1) & 3] >> (16 * (i & 1))));
-    }
-#pragma unroll
-    for (int i = 0; i < 16; i += 2)
-      *(double2*)&xs[xr][xc + i] = double2{ok ? (double)v[i] : 0.0, ok ? (double)v[i + 1] : 0.0};
-  }
-  __syncthreads();
-  route_gemv<kMaxRows>(a, xs, gv, hc, hn, e, lane, 0);
-}
-
 // N 32-bit words from p (16-byte aligned when N % 4 == 0, else 8-byte aligned), loaded
 // as 16- or 8-byte vectors.
 template <int N>
@@ -143,6 +96,54 @@ __device__ __forceinline__ void store_words(void* p, const uint32_t (&w)[N]) {
 #pragma unroll
     for (int q = 0; q < N / 2; q++) ((uint2*)p)[q] = uint2{w[2 * q], w[2 * q + 1]};
   }
+}
+
+// Workgroup (row group, group of 4 experts, 512-input chunk): rows r0 .. r0 + RS - 1 of
+// the window as doubles in LDS, then every wave's expert against them. Fewer rows per
+// workgroup: less work before each workgroup's partials, more reads of the router's
+// weights (from L2 after the first).
+template <bool F32IN, int RS>
+__global__ __launch_bounds__(kRouteThreads) void k_route_logits(RouteArgs a) {
+  constexpr int V = RS * kRouteChunk / kRouteThreads;   // inputs of the piece per thread
+  constexpr int SEG = kRouteChunk / V;                   // threads per row
+  static_assert(V >= 4 && V % 4 == 0, "whole 8- or 16-byte vectors of x");
+  __shared__ __align__(16) double xs[RS][kRouteChunk];
+
+  const int H = a.hidden, R = a.rows, E = a.n_experts;
+  const int n_hc = (H + kRouteChunk - 1) / kRouteChunk;
+  const int n_eg = (E + kRouteWaves - 1) / kRouteWaves;
+  const int hc = blockIdx.x % n_hc, eg = (blockIdx.x / n_hc) % n_eg, rg = blockIdx.x / (n_hc * n_eg);
+  const int h0 = hc * kRouteChunk, r0 = rg * RS;
+  const int hn = min(kRouteChunk, H - h0);   // a multiple of 32 (hidden % 32 == 0), so of V
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int e = eg * kRouteWaves + wave;
+
+  float2 gv[kRouteNU];
+  gate_chunk_load(a, e, h0, hn, lane, gv);
+  // the piece of the window's rows, as doubles (exact): thread t converts row r0 + t / SEG,
+  // inputs V (t % SEG) .. + V - 1; rows past R and inputs past hn become 0
+  {
+    const int xr = tid / SEG, xc = V * (tid % SEG);
+    const bool ok = r0 + xr < R && xc < hn;
+    const long base = (long)min(r0 + xr, R - 1) * H + h0 + min(xc, hn - V);
+    float v[V];
+    if constexpr (F32IN) {
+      uint32_t w[V];
+      load_words<V>((const float*)a.x + base, w);
+#pragma unroll
+      for (int i = 0; i < V; i++) v[i] = __uint_as_float(w[i]);
+    } else {
+      uint32_t w[V / 2];
+      load_words<V / 2>((const uint16_t*)a.x + base, w);
+#pragma unroll
+      for (int i = 0; i < V; i++) v[i] = bf16_to_f32((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+    }
+#pragma unroll
+    for (int i = 0; i < V; i += 2)
+      *(double2*)&xs[xr][xc + i] = double2{ok ? (double)v[i] : 0.0, ok ? (double)v[i + 1] : 0.0};
+  }
+  __syncthreads();
+  route_gemv<RS>(a, xs, gv, hc, hn, e, lane, r0);
 }
 
 // A stack's hand-over between two layers in one launch: layer l's combine over one
@@ -340,25 +341,31 @@ int launch_combine_route(const CombineRouteArgs& c, int res_f32, hipStream_t str
   return (int)hipGetLastError();
 }
 
-int launch_route_logits(const RouteArgs& a, hipStream_t stream, const Prof* p) {
+#ifndef SW_RL_ROWS
+#define SW_RL_ROWS 2
+#endif
+constexpr int kRlRows = SW_RL_ROWS;       // window rows per workgroup of the router's GEMV
+
+static void launch_logits(const RouteArgs& a, hipStream_t stream, const Prof* p) {
   const int n_hc = (a.hidden + kRouteChunk - 1) / kRouteChunk;
   const int n_eg = (a.n_experts + kRouteWaves - 1) / kRouteWaves;
+  const int n_rg = (a.rows + kRlRows - 1) / kRlRows;
+  const dim3 grid(n_hc * n_eg * n_rg);
   if (a.x_dtype == 0)
-    launch(k_route_logits<true>, dim3(n_hc * n_eg), dim3(256), 0, stream, p, a);
+    launch(k_route_logits<true, kRlRows>, grid, dim3(kRouteThreads), 0, stream, p, a);
   else
-    launch(k_route_logits<false>, dim3(n_hc * n_eg), dim3(256), 0, stream, p, a);
+    launch(k_route_logits<false, kRlRows>, grid, dim3(kRouteThreads), 0, stream, p, a);
+}
+
+int launch_route_logits(const RouteArgs& a, hipStream_t stream, const Prof* p) {
+  launch_logits(a, stream, p);
   return (int)hipGetLastError();
 }
 
 int launch_route(const RouteArgs& a, hipStream_t stream, const Prof* p) {
-  const int n_hc = (a.hidden + kRouteChunk - 1) / kRouteChunk;
-  const int n_eg = (a.n_experts + kRouteWaves - 1) / kRouteWaves;
   Prof p0, p1;
   if (p) { p0.start = p->start; p1.stop = p->stop; }
-  if (a.x_dtype == 0)
-    launch(k_route_logits<true>, dim3(n_hc * n_eg), dim3(256), 0, stream, p ? &p0 : nullptr, a);
-  else
-    launch(k_route_logits<false>, dim3(n_hc * n_eg), dim3(256), 0, stream, p ? &p0 : nullptr, a);
+  launch_logits(a, stream, p ? &p0 : nullptr);
   if (a.n_experts <= 2 * kWave)
     launch(k_route_final<2>, dim3(1), dim3(kRouteCoreThreads), 0, stream, p ? &p1 : nullptr, a);
   else
