@@ -145,6 +145,15 @@ __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
+// v summed over the 4 lanes of its quad, by two DPP quad permutes (lane ^ 1, then
+// lane ^ 2): every lane of the quad gets (v0 + v1) + (v2 + v3) or the same terms in the
+// other order, which is the same float. All 4 lanes must be active.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __uint_as_float(dpp32<0xB1>(__float_as_uint(v)));   // quad_perm [1,0,3,2]
+  v += __uint_as_float(dpp32<0x4E>(__float_as_uint(v)));   // quad_perm [2,3,0,1]
+  return v;
+}
+
 // A value of N 32-bit words, permuted word by word.
 template <int N>
 struct Words {

@@ -161,10 +161,8 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(HeadArgs a) {
       shi += (float)hi[e];
       slo += (float)lo[e];
     }
-    shi += __shfl_xor(shi, 1);
-    shi += __shfl_xor(shi, 2);
-    slo += __shfl_xor(slo, 1);
-    slo += __shfl_xor(slo, 2);
+    shi = quad_sum(shi);
+    slo = quad_sum(slo);
     if (ok) {
       f16x8 ph, pl;
 #pragma unroll

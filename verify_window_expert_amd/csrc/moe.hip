@@ -83,10 +83,8 @@ __device__ __forceinline__ void stage_group(const ActLds& l, bool ok, int j, int
     shi += hv;
     slo += bf16_to_f32(lo[e]);
   }
-  shi += __shfl_xor(shi, 1);
-  shi += __shfl_xor(shi, 2);
-  slo += __shfl_xor(slo, 1);
-  slo += __shfl_xor(slo, 2);
+  shi = quad_sum(shi);
+  slo = quad_sum(slo);
   if (ok) {
     u32x4 ph, pl;
 #pragma unroll
@@ -173,8 +171,7 @@ __device__ __forceinline__ void stage_group_bf16(const ActLds& l, bool ok, int j
     const uint32_t word = w[e >> 1];
     shi += __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
   }
-  shi += __shfl_xor(shi, 1);
-  shi += __shfl_xor(shi, 2);
+  shi = quad_sum(shi);
   if (ok) {
     *(u32x4*)(l.xs + (size_t)j * l.stride + 8 * u) = ph;
     if ((u & 3) == 0) l.sx[(u >> 2) * 16 + j] = shi;
@@ -199,10 +196,8 @@ __device__ __forceinline__ void stage_group_hl(const ActLds& l, bool ok, int j, 
     shi += __uint_as_float(word << 16);
     slo += __uint_as_float(word & 0xFFFF0000u);
   }
-  shi += __shfl_xor(shi, 1);
-  shi += __shfl_xor(shi, 2);
-  slo += __shfl_xor(slo, 1);
-  slo += __shfl_xor(slo, 2);
+  shi = quad_sum(shi);
+  slo = quad_sum(slo);
   if (ok) {
     *(u32x4*)(l.xs + (size_t)j * l.stride + 8 * u) = ph;
     *(u32x4*)(l.xs + (size_t)(8 + j) * l.stride + 8 * u) = pl;
@@ -802,17 +797,22 @@ static int compute_units() {
   return cus;
 }
 
+// Workgroups of `kernel` one compute unit holds at this block and LDS size (at least 1).
 template <auto kernel>
-static int persistent_grid(int threads, size_t lds, int max_items, int per_cu_max) {
+static int per_cu(int threads, size_t lds) {
   static size_t cached_lds = 0;
-  static int resident = 0;
-  if (!resident || cached_lds != lds) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
-      per_cu = 1;
-    resident = compute_units() * (per_cu < per_cu_max ? per_cu : per_cu_max);
+  static int n = 0;
+  if (!n || cached_lds != lds) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n <= 0) n = 1;
     cached_lds = lds;
   }
+  return n;
+}
+
+template <auto kernel>
+static int persistent_grid(int threads, size_t lds, int max_items, int per_cu_max) {
+  const int n = per_cu<kernel>(threads, lds);
+  const int resident = compute_units() * (n < per_cu_max ? n : per_cu_max);
   return max_items < resident ? max_items : resident;
 }
 
@@ -836,8 +836,13 @@ template <int BITS, bool F32IN, int XG, bool ROUTED>
 static int launch_gateup_k(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
   auto kern = k_gateup<BITS, F32IN, XG, ROUTED>;
   if (int e = set_lds<k_gateup<BITS, F32IN, XG, ROUTED>>(lds)) return e;
-  // the fused layer: one more workgroup, which writes the routing outputs
-  const int grid = persistent_grid<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds, items, 1) + (ROUTED ? 1 : 0);
+  // the fused layer: one more workgroup, which writes the routing outputs. When a compute
+  // unit holds only one of these workgroups, the items get one compute unit fewer, so
+  // that the extra one starts with the others instead of after the first to finish.
+  int grid = persistent_grid<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds, items, 1);
+  if (ROUTED && per_cu<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds) < 2 && grid >= compute_units())
+    grid = compute_units() - 1;
+  grid += ROUTED ? 1 : 0;
   launch(kern, dim3(grid), dim3(kGuThreads), lds, s, p, a);
   return 0;
 }

@@ -73,8 +73,12 @@ struct RouteLds {
   int n_active;
 };
 
+// Candidate u of a lane: expert u * 64 + lane, so that each of a wave's loads of the
+// partials reads 64 consecutive experts (512 contiguous bytes).
+__device__ __forceinline__ int cand_expert(int u, int lane) { return u * kWave + lane; }
+
 // The partials of row `wave` (waves < rows) and the bias, in registers: lane l holds
-// experts MU*l .. MU*l + MU - 1, chunks 0..7 (a router of more than 8 chunks is read
+// experts cand_expert(0..MU-1, l), chunks 0..7 (a router of more than 8 chunks is read
 // later, in route_select).
 template <int MU>
 struct RouteRegs {
@@ -98,7 +102,7 @@ __device__ __forceinline__ void route_load(const RouteArgs& a, RouteRegs<MU>& g)
   if (wave < R) {
 #pragma unroll
     for (int u = 0; u < MU; u++) {
-      const int ee = min(MU * lane + u, E - 1);
+      const int ee = min(cand_expert(u, lane), E - 1);
 #pragma unroll
       for (int c = 0; c < 8; c++)
         if (c < n_hc) g.part[u][c] = a.partials[((long)c * R + r) * E + ee];
@@ -112,8 +116,8 @@ __device__ __forceinline__ void route_load(const RouteArgs& a, RouteRegs<MU>& g)
 // `out`, also the weights, and writes the tables, the top-k and the weights to a's
 // outputs. Ends with a barrier.
 //
-// Wave r handles row r: lane l holds experts MU*l .. MU*l + MU - 1, each as one unsigned
-// 64-bit key (select_key: larger logit first, ties to the lower index; keys are
+// Wave r handles row r: lane l holds experts cand_expert(u, l), u < MU, each as one
+// unsigned 64-bit key (select_key: larger logit first, ties to the lower index; keys are
 // distinct). The k largest keys are those at or above a threshold found by binary search
 // on the keys' upper 32 bits (each step counts the candidates at or above a trial value
 // with ballots), and, only when several keys share the boundary's upper half, by a
@@ -137,7 +141,7 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
     uint64_t hk[MU];
 #pragma unroll
     for (int u = 0; u < MU; u++) {
-      const int ee = MU * lane + u;
+      const int ee = cand_expert(u, lane);
       double sum = 0.0;
 #pragma unroll
       for (int c = 0; c < 8; c++)
@@ -218,7 +222,7 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
       double zl = 0.0;
 #pragma unroll
       for (int u = 0; u < MU; u++) {
-        ex[u] = MU * lane + u < E ? exp_nonpos(l[u] - lmax) : 0.f;
+        ex[u] = cand_expert(u, lane) < E ? exp_nonpos(l[u] - lmax) : 0.f;
         zl += (double)ex[u];
       }
       const double z = wave_sum(zl);
@@ -238,7 +242,7 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
 #pragma unroll
       for (int u = 0; u < MU; u++) {
         if (sel[u]) {
-          const int e = MU * lane + u;
+          const int e = cand_expert(u, lane);
           a.topk_idx[r * K + rank[u]] = e;
           a.topk_w[r * K + rank[u]] = (float)w[u];
           s.wt[r][e] = (float)w[u];
@@ -248,7 +252,7 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
     } else {
 #pragma unroll
       for (int u = 0; u < MU; u++)
-        if (sel[u]) atomicOr(&s.mask[MU * lane + u], 1u << r);
+        if (sel[u]) atomicOr(&s.mask[cand_expert(u, lane)], 1u << r);
     }
   }
   __syncthreads();
