@@ -277,15 +277,20 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
     before += lanes_below(plane) << b;
     wave_cnt += __popcll(plane) << b;
   }
-  // per row r: the experts of row r below this one (its position in the row's list)
-  uint64_t brow[kMaxRows];
+  // per row r: the experts of row r below this one (its position in the row's list;
+  // only the workgroup that writes the routing outputs needs it)
+  uint64_t brow[kMaxRows] = {};
+  if (out) {
 #pragma unroll
-  for (int rr = 0; rr < kMaxRows; rr++) brow[rr] = __ballot((m >> rr) & 1u);
+    for (int rr = 0; rr < kMaxRows; rr++) brow[rr] = __ballot((m >> rr) & 1u);
+  }
   if (lane == 0 && wave < 4) {
     s.tot[0][wave] = __popcll(bu);
     s.tot[1][wave] = wave_cnt;
+    if (out) {
 #pragma unroll
-    for (int rr = 0; rr < kMaxRows; rr++) s.rowcnt[wave][rr] = __popcll(brow[rr]);
+      for (int rr = 0; rr < kMaxRows; rr++) s.rowcnt[wave][rr] = __popcll(brow[rr]);
+    }
   }
   __syncthreads();
   if (wave < 4) {
@@ -299,14 +304,16 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
     const int K1 = K + 1;
     // this expert's place in each row's list: experts of that row in lower waves + below
     // this lane in its wave
-    int place[kMaxRows];
+    int place[kMaxRows] = {};
+    if (out) {
 #pragma unroll
-    for (int rr = 0; rr < kMaxRows; rr++) {
-      int p = lanes_below(brow[rr]);
+      for (int rr = 0; rr < kMaxRows; rr++) {
+        int p = lanes_below(brow[rr]);
 #pragma unroll
-      for (int w = 0; w < 3; w++)
-        if (w < wave) p += s.rowcnt[w][rr];
-      place[rr] = p;
+        for (int w = 0; w < 3; w++)
+          if (w < wave) p += s.rowcnt[w][rr];
+        place[rr] = p;
+      }
     }
     if (used) {
       const int pos = pf + rank, off = pc + before;
