@@ -374,8 +374,9 @@ template <>
 struct RouteLdsIf<false> {};
 
 // ROUTED: the fused layer. Every workgroup runs the routing core (route_core.h) on the
-// router's partials and takes the window's tables from its own LDS (workgroup 0 also
-// writes the routing outputs); otherwise the tables come from strata_route_out.
+// router's partials and takes the window's tables from its own LDS (one more
+// workgroup, the last, writes the routing outputs and owns no items); otherwise the
+// tables come from strata_route_out.
 template <int BITS, bool F32IN, int XG, bool ROUTED>
 __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   constexpr int DEPTH = kGuDepth;

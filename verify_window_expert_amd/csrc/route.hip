@@ -6,7 +6,8 @@
 // them; the row lists built here are what lets the expert kernels do that.
 //
 // Two launches. k_route_logits: workgroup (row group, expert group, input chunk), each of
-// its 4 waves owns one expert and 512 inputs and writes one double partial per row.
+// its 4 waves owns one expert and 512 inputs and writes one double partial per row of
+// its row group.
 // k_route_final (one workgroup) adds the partials in chunk order, then runs softmax,
 // top-k and grouping for the whole window. (A completion ticket in one launch would
 // serialise one device-scope atomic per workgroup, which costs more than the launch.)
