@@ -261,13 +261,14 @@ int strata_window_tier(void* stream, const uint8_t* row_mask, int n_experts, flo
 
 /*
  * strata_window_stream_read - a plain streaming read of `bytes` bytes at `src` (16-byte
- * words, non-temporal, a grid of 8 workgroups per compute unit): the bandwidth that HBM
+ * words, non-temporal; every wave one contiguous chunk with 16 loads per lane in flight,
+ * 32 waves per compute unit): the bandwidth that HBM
  * actually delivers to a read, against which the layer's kernels are compared (the
  * roofline of the layer is this read of its weights). Measurement only; it computes
  * nothing of the layer.
  *   src   device, 16-byte aligned, bytes a nonzero multiple of 16
- *   sink  device uint32 [1]: written only when the xor of every word equals magic, so
- *         the caller chooses whether anything is written at all
+ *   sink  device uint32 [1]: written (with magic) only when the xor of the words one
+ *         lane reads equals magic, so the caller chooses whether anything is written
  *   prof_events: NULL or {start, end} events recorded by the dispatch.
  * Errors: STRATA_EINVAL for NULL / misaligned pointers or a bad size.
  */

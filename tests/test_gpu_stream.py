@@ -1,5 +1,6 @@
 """The streaming-read yardstick (strata_window_stream_read): it reads every word it is
-given, and writes its sink only when the fold of the words matches the caller's value."""
+given (the last one included, at ragged sizes), and writes its sink only when the fold
+of one lane's words matches the caller's value."""
 import pytest
 import torch
 
@@ -23,9 +24,13 @@ def test_stream_read_folds_every_word(nbytes):
     sw.strata_window_stream_read(src, sink, magic=0)
     torch.cuda.synchronize()
     assert sink[0].item() == 0
-    # one nonzero word (the last): only the thread that reads it folds to its value
-    src[-4:] = torch.tensor([5, 6, 7, 9], dtype=torch.int32, device="cuda")
-    sink.fill_(-1)
-    sw.strata_window_stream_read(src, sink, magic=5 ^ 6 ^ 7 ^ 9)
-    torch.cuda.synchronize()
-    assert sink[0].item() == 5 ^ 6 ^ 7 ^ 9
+    # one nonzero 16-byte word (the first, one in the middle, the last): only the lane that
+    # reads it folds to its value
+    words = nbytes // 16
+    for w in sorted({0, words // 2, words - 1}):
+        src.zero_()
+        src[4 * w:4 * w + 4] = torch.tensor([5, 6, 7, 9], dtype=torch.int32, device="cuda")
+        sink.fill_(-1)
+        sw.strata_window_stream_read(src, sink, magic=5 ^ 6 ^ 7 ^ 9)
+        torch.cuda.synchronize()
+        assert sink[0].item() == 5 ^ 6 ^ 7 ^ 9, w

@@ -360,7 +360,7 @@ def strata_window_accept(argmax, proposal=None, mtp=True, tokens=None, n_tokens=
 def strata_window_stream_read(src, sink, magic=0x9E3779B9, stream=None, prof=None):
     """A plain streaming read of the device tensor src (all its bytes; a nonzero multiple of
     16): the bandwidth yardstick. sink: a device tensor of at least 4 bytes, written only if
-    the xor of every 16-byte word of src equals magic."""
+    the xor of the 16-byte words that one lane reads equals magic."""
     _need(src, "src"); _need(sink, "sink")
     _check(library().strata_window_stream_read(_stream(stream), _ptr(src), src.numel() * src.element_size(),
                                                _ptr(sink), int(magic) & 0xFFFFFFFF, _events(prof)))

@@ -15,6 +15,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxRows = 8;
 constexpr int kMaxTopk = 8;
+// word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle
+constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kCounterBytes = 4096;
 
 // ---------------------------------------------------------------- number formats

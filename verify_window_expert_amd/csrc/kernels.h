@@ -81,7 +81,8 @@ struct CombineRouteArgs {
 
 struct StreamArgs {
   const void* src; size_t words;   // 16-byte words
-  uint32_t* sink; uint32_t magic;  // written only if the fold of every word equals magic
+  uint32_t* sink; uint32_t magic;  // written only if the fold of a wave's words equals magic
+  size_t chunk;                    // set by the launcher: bytes per wave
 };
 
 // Optional timing events of one launch (both may be null): recorded by the dispatch

@@ -258,8 +258,6 @@ struct TileRsrc {
   __amdgpu_buffer_rsrc_t codes, meta;
 };
 
-// word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle
-constexpr int kRsrcWord3 = 0x00020000;
 
 // An expert id read at run time, clamped into [0, E] (E = the shared expert), so that
 // a load is always inside the weights even for an unspecified table entry.
