@@ -185,9 +185,12 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
  * strata_window_layer - the whole MoE layer of one window in one call: what
  * strata_window_route and then strata_window_moe compute, with the same arguments and
  * outputs (route receives the window's routing, as strata_window_route writes it), in
- * three kernels instead of five: the router's GEMV, then gate/up whose every workgroup
+ * four kernels instead of five: the router's GEMV, then gate/up whose every workgroup
  * takes top-k, softmax and grouping from the GEMV's partial sums itself, then down and
- * the combine. (Strata docs/BATCHING.md, opening paragraph: the router, the shared expert
+ * the combine. Where the activations and the routing tables do not fit one compute
+ * unit's LDS together (bf16 activations above about 7,600 hidden, float above about
+ * 4,200), the call runs the routing as a kernel of its own, as strata_window_route does,
+ * and the plain gate/up: the same results. (Strata docs/BATCHING.md, opening paragraph: the router, the shared expert
  * and every routed expert the rows use are read once per window for all of them.)
  *   ws: at least strata_window_workspace(3, ...) bytes.
  * Errors: those of strata_window_route and strata_window_moe, and a workspace smaller

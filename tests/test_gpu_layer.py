@@ -89,3 +89,10 @@ def test_layer_matches_two_call_path():
         assert np.array_equal(gr1[k], gr2[k]), k
     np.testing.assert_allclose(gr1["topk_w"], gr2["topk_w"], rtol=1e-6)
     assert row_rel_err(o1, o2) <= 1e-5
+
+
+def test_layer_hidden_beyond_the_fused_lds():
+    """hidden 7936 (bf16): the activation image and the routing core's tables do not fit
+    one compute unit's LDS together, so the layer call runs the routing as a kernel of its
+    own and the plain gate/up; the same results."""
+    check(synth.config("two_slots_mtp", hidden=7936, ffn=256, experts=16, top_k=4, rows=3), 0)

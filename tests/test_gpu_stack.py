@@ -122,3 +122,10 @@ def test_stack24_head_full():
     """The layer-stack workload at its full size: 24 layers and the vocab-151936 head."""
     cfg = synth.config("stack24_head")
     check_stack(cfg, cfg.layers, head=True, oracle_layers=(0, 23))
+
+
+def test_stack_hidden_beyond_the_fused_lds():
+    """hidden 7936 (bf16): every layer takes the routing as a kernel of its own and the
+    plain gate/up after the fused hand-over; still bit-identical to the layer calls."""
+    cfg = synth.config("two_slots_mtp", hidden=7936, ffn=256, experts=16, top_k=4, rows=3)
+    check_stack(cfg, 2, oracle_layers=(0, 1))

@@ -135,6 +135,12 @@ int check_qmat(const strata_qmat* q, const char* name, int rows, int cols, int n
   return STRATA_OK;
 }
 
+// Whether the fused gate/up (routing core + activation image in one workgroup's LDS)
+// fits; else the layer runs the routing core as a kernel of its own and the plain gate/up.
+bool fused_fits(int hidden, int x_dtype) {
+  return sw::gateup_lds_bytes(hidden, x_dtype) + kStaticLds + sw::route_core_lds_bytes() <= kLdsLimit;
+}
+
 int launch_status(int rc, const char* what) {
   if (rc == 0) return STRATA_OK;
   return fail(STRATA_EHIP, "%s launch failed: %s", what, hipGetErrorString((hipError_t)rc));
@@ -317,16 +323,20 @@ int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int 
   if ((rc = prepare_moe(x, x_dtype, rows, hidden, ffn, gate, up, down, sh_gate, sh_up, sh_down, route, n_experts,
                         top_k, residual, out, x_next_bf16, ws, w.moe, g, d, max_slots)))
     return rc;
-  if (sw::gateup_lds_bytes(hidden, x_dtype) + kStaticLds + sw::route_core_lds_bytes() > kLdsLimit)
-    return fail(STRATA_EUNSUPPORTED, "hidden %d: the activations and the routing tables need more than %zu bytes "
-                "of LDS (use strata_window_route and strata_window_moe)", hidden, kLdsLimit);
   if (ws_bytes < w.total) return fail(STRATA_EINVAL, "layer workspace %zu < %zu bytes", ws_bytes, w.total);
   g.route = r;
   hipStream_t s = (hipStream_t)stream;
   const sw::Prof pr = prof(prof_events, 0), pg = prof(prof_events, 2), pd = prof(prof_events, 4);
-  if ((rc = launch_status(sw::launch_route_logits(r, s, prof_events ? &pr : nullptr), "router"))) return rc;
-  if ((rc = launch_status(sw::launch_gateup_routed(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up")))
-    return rc;
+  if (fused_fits(hidden, x_dtype)) {
+    if ((rc = launch_status(sw::launch_route_logits(r, s, prof_events ? &pr : nullptr), "router"))) return rc;
+    if ((rc = launch_status(sw::launch_gateup_routed(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up")))
+      return rc;
+  } else {
+    // the activation image leaves no room for the routing core's tables: the routing
+    // core runs as a kernel of its own (as strata_window_route), then the plain gate/up
+    if ((rc = launch_status(sw::launch_route(r, s, prof_events ? &pr : nullptr), "router"))) return rc;
+    if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
+  }
   return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
 }
 
@@ -372,9 +382,6 @@ int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int 
       snprintf(msg, sizeof msg, "%s", g_err);
       return fail(rc, "layer %d: %s", l, msg);
     }
-    if (sw::gateup_lds_bytes(hidden, input_dtype(l)) + kStaticLds + sw::route_core_lds_bytes() > kLdsLimit)
-      return fail(STRATA_EUNSUPPORTED, "hidden %d: the activations and the routing tables need more than %zu bytes "
-                  "of LDS", hidden, kLdsLimit);
   }
   sw::HeadArgs ha;
   if (head) {
@@ -406,8 +413,15 @@ int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int 
                 w.layer.moe, g, d, max_slots, true);
     g.route = r;
     const bool last_layer = l == n_layers - 1;
+    // layer 0's router GEMV here; every later layer's partials come from the hand-over.
+    // Where the routing core's tables do not fit beside the activations, the routing
+    // core runs as a kernel of its own and gate/up reads its tables.
+    const bool fused = fused_fits(hidden, input_dtype(l));
     if (l == 0 && (rc = launch_status(sw::launch_route_logits(r, s, p_first), "router"))) return rc;
-    if ((rc = launch_status(sw::launch_gateup_routed(g, max_slots, s, nullptr), "gate/up"))) return rc;
+    if (!fused && (rc = launch_status(sw::launch_route_final(r, s, nullptr), "routing"))) return rc;
+    if ((rc = launch_status(fused ? sw::launch_gateup_routed(g, max_slots, s, nullptr)
+                                  : sw::launch_gateup(g, max_slots, s, nullptr), "gate/up")))
+      return rc;
     if ((rc = launch_status(sw::launch_down(d, max_slots, s, last_layer && !head ? p_last : nullptr, last_layer),
                             "down")))
       return rc;

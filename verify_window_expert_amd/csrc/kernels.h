@@ -106,8 +106,10 @@ int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof*
 // the fused layer's gate/up: routing from a.route's partials in every workgroup (one more
 // workgroup writes the routing outputs), then gate/up as launch_gateup
 int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
-// the router's GEMV alone (the fused layer's first kernel)
+// the router's GEMV alone (the fused layer's first kernel), and the routing core alone
+// (top-k, softmax, grouping from the GEMV's partials: one workgroup)
 int launch_route_logits(const RouteArgs& a, hipStream_t s, const Prof* p);
+int launch_route_final(const RouteArgs& a, hipStream_t s, const Prof* p);
 // down, then (combine) the combine kernel
 int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p, bool combine = true);
 // layer l's combine and layer l + 1's router GEMV in one launch (res_f32: layer l's input is float)

@@ -363,6 +363,14 @@ int launch_route_logits(const RouteArgs& a, hipStream_t stream, const Prof* p) {
   return (int)hipGetLastError();
 }
 
+int launch_route_final(const RouteArgs& a, hipStream_t stream, const Prof* p) {
+  if (a.n_experts <= 2 * kWave)
+    launch(k_route_final<2>, dim3(1), dim3(kRouteCoreThreads), 0, stream, p, a);
+  else
+    launch(k_route_final<4>, dim3(1), dim3(kRouteCoreThreads), 0, stream, p, a);
+  return (int)hipGetLastError();
+}
+
 int launch_route(const RouteArgs& a, hipStream_t stream, const Prof* p) {
   Prof p0, p1;
   if (p) { p0.start = p->start; p1.stop = p->stop; }
