@@ -95,11 +95,11 @@ __device__ __forceinline__ bf16x8 q4_to_bf16x8(uint32_t v, const CodeConsts& k) 
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// 2-bit: the 8 codes of one block are 16 bits (code i at bits 2i). Spreading the two
-// bytes into the two halves of a word gives, per shift 2i, codes i and i+4: the same
-// element order as q4_to_bf16x8.
-__device__ __forceinline__ bf16x8 q2_to_bf16x8(uint32_t half16, const CodeConsts& k) {
-  const uint32_t v = (half16 & 0xFFu) | ((half16 & 0xFF00u) << 8);
+// 2-bit: the 8 codes of one block are 16 bits (code i at bits 2i), the low or high half
+// of a code word. One byte permute spreads the half's two bytes into the two halves of
+// a word; then, per shift 2i, codes i and i+4: the same element order as q4_to_bf16x8.
+__device__ __forceinline__ bf16x8 q2_to_bf16x8(uint32_t word, bool high, const CodeConsts& k) {
+  const uint32_t v = __builtin_amdgcn_perm(0u, word, high ? 0x0C030C02u : 0x0C010C00u);
   u32x4 w;
   w[0] = (v & k.m2) | k.magic;
   w[1] = ((v >> 2) & k.m2) | k.magic;

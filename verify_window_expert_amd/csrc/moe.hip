@@ -300,7 +300,7 @@ __device__ __forceinline__ void load_kgroup(KGroup<BITS>& kg, const TileRsrc& r,
 template <int BITS>
 __device__ __forceinline__ bf16x8 code_operand(const KGroup<BITS>& kg, int beta, const CodeConsts& cc) {
   return BITS == 4 ? q4_to_bf16x8(kg.codes[beta], cc)
-                   : q2_to_bf16x8((kg.codes[beta >> 1] >> (16 * (beta & 1))) & 0xFFFFu, cc);
+                   : q2_to_bf16x8(kg.codes[beta >> 1], (beta & 1) != 0, cc);
 }
 
 // Accumulate one k-group of one matrix (or two matrices against the same activations)
