@@ -642,8 +642,10 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   // workgroups of this slot: b = slot + k * n_active, k < nw
   const int k = blockIdx.x / n_active;
   const int nw = (gridDim.x - slot + n_active - 1) / n_active;
-  // this wave's tiles: t = k * 8 + wave + j * (nw * 8)
-  const int stride = nw * kDnWaves, t0 = k * kDnWaves + wave;
+  // this wave's tiles: t = wave * nw + k + j * (nw * 16), one to one onto 0 .. nw * 16 - 1
+  // and its repeats; interleaved so that the slot's tiles spread over all its workgroups
+  // (every compute unit streams) instead of filling the first ones
+  const int stride = nw * kDnWaves, t0 = wave * nw + k;
   const int my_tiles = t0 < tiles_h ? (tiles_h - t0 + stride - 1) / stride : 0;
   const int units = my_tiles * NG;
 
