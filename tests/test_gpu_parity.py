@@ -177,6 +177,22 @@ def test_window_row_equals_row_alone_bitwise(name):
         assert np.array_equal(o1[0], gout[r]), (r, np.max(np.abs(o1[0] - gout[r])))
 
 
+def test_window_row_equals_row_alone_bitwise_f32():
+    """float32 input (bf16 hi and lo columns) at hidden 1024, whose 8 k-groups split over
+    two waves per gate/up item: each row of a full window (~40 experts) equals that row run
+    as a 1-row window, bit for bit, through both entry paths."""
+    cfg = synth.config("small_f32", hidden=1024, ffn=768, experts=64, top_k=8, rows=8)
+    check_window(cfg, 0)
+    L, dl, mats = layer_for(cfg)
+    x = synth.make_window(cfg, 3)
+    gr, gout, _ = gpu_window(dl, to_dev_x(x), cfg.top_k)
+    for layer in (False, True):
+        for r in range(cfg.rows):
+            g1, o1, _ = gpu_window(dl, to_dev_x(x[r:r + 1]), cfg.top_k, layer=layer)
+            assert np.array_equal(g1["topk_idx"][0], gr["topk_idx"][r])
+            assert np.array_equal(o1[0], gout[r]), (layer, r, np.max(np.abs(o1[0] - gout[r])))
+
+
 def test_run_to_run_deterministic():
     cfg = synth.config("four_slots_mtp_zipf")
     L, dl, mats = layer_for(cfg)
