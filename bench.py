@@ -314,7 +314,7 @@ def cpu_baseline(cfg, host_layer, seconds, threads=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the window is measured on one GPU: the path has no multi-GPU mode (--gpus must be 1)"}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
