@@ -13,7 +13,11 @@
  * is alone or grouped with others.
  *
  * Conventions for every entry point
- *   - Stateless: the library keeps no state between calls.
+ *   - Stateless: the library keeps no data between calls; it caches only launch
+ *     parameters per process (the GPU's compute-unit count, each kernel's occupancy and
+ *     raised LDS limit), so every GPU one process drives must be the same model.
+ *   - Threads: entry points may be called from several host threads at once (the caches
+ *     are locked; the error string is per thread), each call with its own workspace.
  *   - Every pointer argument except `stream` and the descriptor structs themselves is a
  *     DEVICE pointer owned by the caller, valid until the work enqueued on `stream` has
  *     finished. The descriptor structs (strata_qmat, strata_route_out) are read on the

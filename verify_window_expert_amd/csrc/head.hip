@@ -12,6 +12,7 @@
 //     sum_k w x = scale * (D - 1152 * Sx),  D = sum (1152 + q) x.
 // A second one-workgroup launch reduces the per-workgroup argmax candidates.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -311,7 +312,9 @@ int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p) {
 
 template <bool F32IN, int XG>
 static int launch_head_k(const HeadArgs& a, size_t lds, int nwg, hipStream_t s, const Prof* p) {
+  static std::mutex m;
   static size_t granted = 64 * 1024;   // raise the dynamic LDS limit once, when needed
+  std::lock_guard<std::mutex> lock(m);
   if (lds > granted) {
     if (int e = (int)hipFuncSetAttribute((const void*)k_head<F32IN, XG>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)lds))

@@ -23,6 +23,7 @@
 // read once, in parallel, into LDS.
 #include "route_core.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace sw {
@@ -786,14 +787,19 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DownArgs a) {
 
 // Persistent grids: resident workgroups per compute unit (occupancy of the kernel at
 // this block and LDS size, capped by per_cu_max) times the compute units, never more
-// than the window can use. Cached per kernel and LDS size.
+// than the window can use. Cached per kernel and LDS size, once per process (every GPU
+// a process drives is taken to be the same model); the caches are locked, so host
+// threads may launch at once.
 static int compute_units() {
+  static std::mutex m;
   static int cus = 0;
+  std::lock_guard<std::mutex> lock(m);
   if (!cus) {
-    int dev = 0;
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
   }
   return cus;
 }
@@ -801,8 +807,10 @@ static int compute_units() {
 // Workgroups of `kernel` one compute unit holds at this block and LDS size (at least 1).
 template <auto kernel>
 static int per_cu(int threads, size_t lds) {
+  static std::mutex m;
   static size_t cached_lds = 0;
   static int n = 0;
+  std::lock_guard<std::mutex> lock(m);
   if (!n || cached_lds != lds) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n <= 0) n = 1;
     cached_lds = lds;
@@ -821,7 +829,9 @@ static int persistent_grid(int threads, size_t lds, int max_items, int per_cu_ma
 // per process and kernel; the attribute only grows).
 template <auto kernel>
 static int set_lds(size_t bytes) {
+  static std::mutex m;
   static size_t granted = 0;
+  std::lock_guard<std::mutex> lock(m);
   if (bytes <= granted) return 0;
   hipFuncAttributes fa;
   if (int e = (int)hipFuncGetAttributes(&fa, (const void*)kernel)) return e;
