@@ -96,3 +96,33 @@ def test_layer_hidden_beyond_the_fused_lds():
     one compute unit's LDS together, so the layer call runs the routing as a kernel of its
     own and the plain gate/up; the same results."""
     check(synth.config("two_slots_mtp", hidden=7936, ffn=256, experts=16, top_k=4, rows=3), 0)
+
+
+def test_binding_refuses_short_or_mismatched_buffers():
+    """The library sees only pointers, so the binding refuses, before anything is enqueued,
+    caller buffers that the kernels would access past their end (or read with the wrong
+    type), and routing outputs made for another window shape; the call then still works."""
+    cfg = synth.config("small_f32")
+    L, dl, mats = layer_for(cfg)
+    x = to_dev_x(synth.make_window(cfg, 0))
+    R, H, E, k = cfg.rows, cfg.hidden, cfg.experts, cfg.top_k
+    f32 = dict(dtype=torch.float32, device="cuda")
+    layer = lambda **kw: sw.strata_window_layer(x, dl.gate_w, dl.bias, k, dl.gate, dl.up, dl.down, *dl.sh, **kw)
+    with pytest.raises(ValueError):
+        layer(out=torch.empty(R, H - 32, **f32))
+    with pytest.raises(TypeError):
+        layer(x_next=torch.empty(R, H, **f32))
+    with pytest.raises(ValueError):
+        layer(route=sw.RouteOut(R + 1, E, k))
+    with pytest.raises(ValueError):
+        sw.strata_window_route(x, dl.gate_w[:, : H - 32].contiguous(), dl.bias, k)
+    with pytest.raises(ValueError):
+        sw.strata_window_moe(x, dl.gate, dl.up, dl.down, *dl.sh, sw.RouteOut(R, E, k), residual=x[:1])
+    with pytest.raises(ValueError):
+        sw.QMat(dl.gate.codes[:, :-16].contiguous(), dl.gate.meta, dl.gate.rows, dl.gate.cols, dl.gate.bits)
+    with pytest.raises(ValueError):
+        sw.strata_window_accept(torch.zeros(4, dtype=torch.int32, device="cuda"),
+                                torch.zeros(1, dtype=torch.int32, device="cuda"))
+    out, ro = layer()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()

@@ -121,6 +121,59 @@ def _need(t, name, device=None):
     return t
 
 
+def _need_buf(t, name, dtype, numel):
+    """A caller-supplied device tensor the kernels read or write: contiguous, of dtype, with
+    at least numel elements. The library sees only its pointer, so a short buffer would be
+    accessed past its end; it is refused here, before anything is enqueued."""
+    _need(t, name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    return t
+
+
+def _need_x(x):
+    _need(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, hidden]")
+    _x_dtype(x)
+    return x.shape
+
+
+def _need_router(gate_w, bias, hidden):
+    _need(gate_w, "gate_w")
+    if gate_w.dtype != torch.float32 or gate_w.dim() != 2 or gate_w.shape[1] != hidden:
+        raise ValueError(f"gate_w must be float32 [n_experts, {hidden}]")
+    if bias is not None:
+        _need_buf(bias, "bias", torch.float32, gate_w.shape[0])
+    return gate_w.shape[0]
+
+
+def _need_route(route, rows, n_experts, top_k, name="route"):
+    if not isinstance(route, RouteOut):
+        raise TypeError(f"{name} must be a RouteOut")
+    if (route.rows, route.n_experts, route.top_k) != (rows, n_experts, top_k):
+        raise ValueError(f"{name} was made for rows {route.rows}, experts {route.n_experts}, top_k {route.top_k}; "
+                         f"the call has {rows}, {n_experts}, {top_k}")
+    return route
+
+
+def _ws_bytes(ws):
+    _need(ws, "ws")
+    return ws.numel() * ws.element_size()
+
+
+def _need_outs(x, rows, hidden, residual, out, x_next):
+    n = rows * hidden
+    if residual is not None:
+        _need_buf(residual, "residual", x.dtype, n)
+    if out is not None:
+        _need_buf(out, "out", torch.float32, n)
+    if x_next is not None:
+        _need_buf(x_next, "x_next", torch.bfloat16, n)
+
+
 class QMat:
     """Device view of one block-quantized matrix, or n_mat stacked ones.
 
@@ -133,6 +186,13 @@ class QMat:
         self.meta = _need(meta, "meta")
         self.rows, self.cols, self.bits = int(rows), int(cols), int(bits)
         self.n_mat = codes.shape[0] if codes.dim() == 2 else 1
+        # every matrix's codes and per-block meta words must be there in full
+        need_c = self.rows * self.cols * self.bits // 8
+        need_m = self.rows * (self.cols // 32) * (2 if self.bits == 8 else 4)
+        if codes.numel() * codes.element_size() < self.n_mat * need_c or \
+                meta.numel() * meta.element_size() < self.n_mat * need_m:
+            raise ValueError(f"codes/meta hold less than {self.n_mat} matrices of {self.rows} x {self.cols} "
+                             f"at {self.bits} bits")
 
     def c(self):
         per_c = self.codes.numel() // self.n_mat
@@ -194,25 +254,23 @@ def workspace_bytes(which, rows, hidden, ffn=0, n_experts=0, top_k=0, vocab=0):
 
 
 def workspace(nbytes, device="cuda"):
-    """A zeroed device workspace (its completion counters must start at zero)."""
+    """A device workspace of at least nbytes (the library needs its contents in no
+    particular state; it is zero-filled here only so that runs start alike)."""
     return torch.zeros(max(int(nbytes), WS_COUNTER_BYTES), dtype=torch.uint8, device=device)
 
 
 def strata_window_route(x, gate_w, bias, top_k, renorm=False, out=None, ws=None, stream=None, prof=None):
     """Router, softmax, top-k and grouping of one window. Returns a RouteOut.
     prof: None or [start, end] hipEvent_t handles recorded around the kernel."""
-    _need(x, "x"); _need(gate_w, "gate_w")
-    if bias is not None:
-        _need(bias, "bias")
-    rows, hidden = x.shape
-    E = gate_w.shape[0]
-    out = RouteOut(rows, E, top_k, x.device) if out is None else out
+    rows, hidden = _need_x(x)
+    E = _need_router(gate_w, bias, hidden)
+    out = RouteOut(rows, E, top_k, x.device) if out is None else _need_route(out, rows, E, top_k, "out")
     if ws is None:
         ws = workspace(workspace_bytes(0, rows, hidden, n_experts=E), x.device)
     ro = out.c()
     _check(library().strata_window_route(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, _ptr(gate_w),
                                          _ptr(bias), E, top_k, STRATA_ROUTE_RENORM if renorm else 0,
-                                         ctypes.byref(ro), _ptr(ws), ws.numel(), _events(prof)))
+                                         ctypes.byref(ro), _ptr(ws), _ws_bytes(ws), _events(prof)))
     return out
 
 
@@ -220,23 +278,20 @@ def strata_window_moe(x, gate, up, down, sh_gate, sh_up, sh_down, route, residua
                       x_next=None, ws=None, stream=None, prof=None):
     """Experts of one window. Returns out [rows, hidden] float32 (x_next filled if given).
     prof: None or [gate/up start, gate/up end, down start, down end] hipEvent_t handles."""
-    _need(x, "x")
-    rows, hidden = x.shape
+    rows, hidden = _need_x(x)
     ffn = gate.rows
+    _need_route(route, rows, route.n_experts, route.top_k)
+    _need_outs(x, rows, hidden, residual, out, x_next)
     if out is None:
         out = torch.empty(rows, hidden, dtype=torch.float32, device=x.device)
     if ws is None:
         ws = workspace(workspace_bytes(1, rows, hidden, ffn, route.n_experts, route.top_k), x.device)
-    if residual is not None:
-        _need(residual, "residual")
-    if x_next is not None:
-        _need(x_next, "x_next")
     qs = [q.c() for q in (gate, up, down, sh_gate, sh_up, sh_down)]
     ro = route.c()
     _check(library().strata_window_moe(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ffn,
                                        *[ctypes.byref(q) for q in qs], ctypes.byref(ro), route.n_experts,
                                        route.top_k, _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws),
-                                       ws.numel(), _events(prof)))
+                                       _ws_bytes(ws), _events(prof)))
     return out
 
 
@@ -245,27 +300,21 @@ def strata_window_layer(x, gate_w, bias, top_k, gate, up, down, sh_gate, sh_up, 
     """The whole layer of one window in one call (router, then experts). Returns
     (out [rows, hidden] float32, the window's RouteOut); x_next filled if given.
     prof: None or [router start, end, gate/up start, end, down start, end] handles."""
-    _need(x, "x"); _need(gate_w, "gate_w")
-    if bias is not None:
-        _need(bias, "bias")
-    rows, hidden = x.shape
-    E = gate_w.shape[0]
+    rows, hidden = _need_x(x)
+    E = _need_router(gate_w, bias, hidden)
     ffn = gate.rows
-    route = RouteOut(rows, E, top_k, x.device) if route is None else route
+    route = RouteOut(rows, E, top_k, x.device) if route is None else _need_route(route, rows, E, top_k)
+    _need_outs(x, rows, hidden, residual, out, x_next)
     if out is None:
         out = torch.empty(rows, hidden, dtype=torch.float32, device=x.device)
     if ws is None:
         ws = workspace(workspace_bytes(3, rows, hidden, ffn, E, top_k), x.device)
-    if residual is not None:
-        _need(residual, "residual")
-    if x_next is not None:
-        _need(x_next, "x_next")
     qs = [q.c() for q in (gate, up, down, sh_gate, sh_up, sh_down)]
     ro = route.c()
     _check(library().strata_window_layer(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ffn, _ptr(gate_w),
                                          _ptr(bias), STRATA_ROUTE_RENORM if renorm else 0,
                                          *[ctypes.byref(q) for q in qs], E, top_k, ctypes.byref(ro),
-                                         _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws), ws.numel(),
+                                         _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws), _ws_bytes(ws),
                                          _events(prof)))
     return out, route
 
@@ -278,9 +327,10 @@ def strata_window_stack(x, layers, top_k, head=None, renorm=False, routes=None, 
     routes: None (one RouteOut shared by all layers) or one RouteOut per layer.
     Returns (x_final bf16 [rows, hidden], the routes list, logits or None, argmax or None);
     out (the last layer's float output) is filled if given."""
-    _need(x, "x")
-    rows, hidden = x.shape
+    rows, hidden = _need_x(x)
     n = len(layers)
+    if n < 1:
+        raise ValueError("at least one layer")
     E = layers[0][0].shape[0]
     ffn = layers[0][2].rows
     if routes is None:
@@ -290,14 +340,16 @@ def strata_window_stack(x, layers, top_k, head=None, renorm=False, routes=None, 
         raise ValueError("one RouteOut per layer, or None")
     cl = (CLayer * n)()
     for i, (gw, bias, *mats) in enumerate(layers):
-        _need(gw, "gate_w")
-        if bias is not None:
-            _need(bias, "bias")
+        if _need_router(gw, bias, hidden) != E:
+            raise ValueError(f"layer {i} has {gw.shape[0]} experts, layer 0 {E}")
+        _need_route(routes[i], rows, E, top_k, f"routes[{i}]")
         cl[i] = CLayer(gw.data_ptr(), None if bias is None else bias.data_ptr(), *[q.c() for q in mats],
                        routes[i].c())
     if x_final is None:
         x_final = torch.empty(rows, hidden, dtype=torch.bfloat16, device=x.device)
-    _need(x_final, "x_final")
+    _need_buf(x_final, "x_final", torch.bfloat16, rows * hidden)
+    if out is not None:
+        _need_buf(out, "out", torch.float32, rows * hidden)
     lg = am = None
     V = 0
     if head is not None:
@@ -306,30 +358,35 @@ def strata_window_stack(x, layers, top_k, head=None, renorm=False, routes=None, 
         if lg is False:
             lg = None
         am = torch.empty(max(rows, 4), dtype=torch.int32, device=x.device) if argmax is None else argmax
+        if lg is not None:
+            _need_buf(lg, "logits", torch.float32, rows * V)
+        _need_buf(am, "argmax", torch.int32, rows)
     if ws is None:
         ws = workspace(workspace_bytes(4, rows, hidden, ffn, E, top_k, V), x.device)
     hq = head.c() if head is not None else None
     _check(library().strata_window_stack(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ffn, E, top_k,
                                          STRATA_ROUTE_RENORM if renorm else 0, n, cl,
                                          None if hq is None else ctypes.byref(hq), V, _ptr(lg), _ptr(am),
-                                         _ptr(out), _ptr(x_final), _ptr(ws), ws.numel(), _events(prof)))
+                                         _ptr(out), _ptr(x_final), _ptr(ws), _ws_bytes(ws), _events(prof)))
     return x_final, routes, lg, (None if am is None else am[:rows])
 
 
 def strata_window_head(x, head, logits=True, argmax=None, ws=None, stream=None, prof=None):
     """Head GEMV and argmax of one window. Returns (logits or None, argmax int32 [rows])."""
-    _need(x, "x")
-    rows, hidden = x.shape
+    rows, hidden = _need_x(x)
     V = head.rows
     lg = torch.empty(rows, V, dtype=torch.float32, device=x.device) if logits is True else logits
     if lg is False:
         lg = None
     am = torch.empty(max(rows, 4), dtype=torch.int32, device=x.device) if argmax is None else argmax
+    if lg is not None:
+        _need_buf(lg, "logits", torch.float32, rows * V)
+    _need_buf(am, "argmax", torch.int32, rows)
     if ws is None:
         ws = workspace(workspace_bytes(2, rows, hidden, vocab=V), x.device)
     q = head.c()
     _check(library().strata_window_head(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, ctypes.byref(q),
-                                        V, _ptr(lg), _ptr(am), _ptr(ws), ws.numel(), _events(prof)))
+                                        V, _ptr(lg), _ptr(am), _ptr(ws), _ws_bytes(ws), _events(prof)))
     return lg, am[:rows]
 
 
@@ -347,10 +404,15 @@ def strata_window_accept(argmax, proposal=None, mtp=True, tokens=None, n_tokens=
         _need(proposal, "proposal")
         if proposal.dtype != torch.int32:
             raise TypeError("proposal must be int32")
+    if mtp:
+        _need_buf(proposal, "proposal", torch.int32, n_slots)
     i32 = dict(dtype=torch.int32, device=argmax.device)
     tokens = torch.empty(n_slots, 2, **i32) if tokens is None else tokens
     n_tokens = torch.empty(n_slots, **i32) if n_tokens is None else n_tokens
     n_accepted = torch.empty(4, **i32) if n_accepted is None else n_accepted
+    _need_buf(tokens, "tokens", torch.int32, 2 * n_slots)
+    _need_buf(n_tokens, "n_tokens", torch.int32, n_slots)
+    _need_buf(n_accepted, "n_accepted", torch.int32, 1)
     _check(library().strata_window_accept(_stream(stream), _ptr(argmax), rows, n_slots, int(bool(mtp)),
                                           _ptr(proposal) if mtp else None, _ptr(tokens), _ptr(n_tokens),
                                           _ptr(n_accepted), _events(prof)))
@@ -362,6 +424,8 @@ def strata_window_stream_read(src, sink, magic=0x9E3779B9, stream=None, prof=Non
     16): the bandwidth yardstick. sink: a device tensor of at least 4 bytes, written only if
     the xor of the 16-byte words that one lane reads equals magic."""
     _need(src, "src"); _need(sink, "sink")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
     _check(library().strata_window_stream_read(_stream(stream), _ptr(src), src.numel() * src.element_size(),
                                                _ptr(sink), int(magic) & 0xFFFFFFFF, _events(prof)))
 
@@ -377,10 +441,12 @@ def strata_window_tier(row_mask, counts, decay=1.0, resident=None, max_swaps=0, 
     if counts.dtype != torch.float32 or row_mask.dtype != torch.uint8 or row_mask.numel() < E:
         raise TypeError("counts must be float32 [E] and row_mask uint8 [E + 1]")
     if resident is not None:
-        _need(resident, "resident")
+        _need_buf(resident, "resident", torch.uint8, E)
         i32 = dict(dtype=torch.int32, device=counts.device)
         swaps = torch.empty(max(max_swaps, 1), 2, **i32) if swaps is None else swaps
         n_swaps = torch.empty(4, **i32) if n_swaps is None else n_swaps
+        _need_buf(swaps, "swaps", torch.int32, 2 * max_swaps)
+        _need_buf(n_swaps, "n_swaps", torch.int32, 1)
     _check(library().strata_window_tier(_stream(stream), _ptr(row_mask), E, _ptr(counts), float(decay),
                                         _ptr(resident), int(max_swaps), float(min_gain), _ptr(swaps),
                                         _ptr(n_swaps), _events(prof)))
