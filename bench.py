@@ -177,18 +177,21 @@ class Steps:
     """Device state of K steps: layers, windows, per-step routing outputs, workspaces."""
 
     def __init__(self, cfg, n_layers, n_windows, steps, sw, torch, synth, DevLayer, to_dev_x, inflight=1,
-                 path="layer"):
+                 path="layer", out_per_step=False, keep_host_layers=False):
         self.cfg, self.sw, self.torch = cfg, sw, torch
         self.path = path
         R, H, E, k = cfg.rows, cfg.hidden, cfg.experts, cfg.top_k
         t0 = time.time()
         self.layers = []
+        self.host_layers = []
         self.host_layer0 = None
         for l in range(n_layers):
             L = synth.make_layer(cfg, l)
             self.layers.append(DevLayer(L, cfg))
             if l == 0:
                 self.host_layer0 = L
+            if keep_host_layers:
+                self.host_layers.append(L)
             log(f"[bench] layer {l + 1}/{n_layers} resident ({time.time() - t0:.1f}s)")
         self.xs = [to_dev_x(synth.make_window(cfg, w, rows=R)) for w in range(n_windows)]
         # per-step routing outputs (so the timed graph holds no copies)
@@ -198,7 +201,10 @@ class Steps:
         self.ws_r = [sw.workspace(sw.workspace_bytes(0, R, H, n_experts=E)) for _ in range(inflight)]
         self.ws_m = [sw.workspace(sw.workspace_bytes(1 if path == "split" else 3, R, H, cfg.ffn, E, k))
                      for _ in range(inflight)]
-        self.out = [torch.empty(R, H, dtype=torch.float32, device=dev) for _ in range(inflight)]
+        # one output per window in flight (each step its own with out_per_step)
+        self.out = [torch.empty(R, H, dtype=torch.float32, device=dev)
+                    for _ in range(steps if out_per_step else inflight)]
+        self.out_per_step = out_per_step
         self.inflight = inflight
 
     def step(self, i, prof=None):
@@ -208,17 +214,39 @@ class Steps:
         dl = self.layers[i % len(self.layers)]
         x = self.xs[i % len(self.xs)]
         j = i % self.inflight
+        out = self.out[i if self.out_per_step else j]
         if self.path == "layer":
             sw.strata_window_layer(x, dl.gate_w, dl.bias, cfg.top_k, dl.gate, dl.up, dl.down, *dl.sh,
-                                   route=self.routes[i], out=self.out[j], ws=self.ws_m[j], prof=prof)
+                                   route=self.routes[i], out=out, ws=self.ws_m[j], prof=prof)
             return
         ro = sw.strata_window_route(x, dl.gate_w, dl.bias, cfg.top_k, out=self.routes[i], ws=self.ws_r[j],
                                     prof=None if prof is None else prof[:2])
-        sw.strata_window_moe(x, dl.gate, dl.up, dl.down, *dl.sh, ro, out=self.out[j], ws=self.ws_m[j],
+        sw.strata_window_moe(x, dl.gate, dl.up, dl.down, *dl.sh, ro, out=out, ws=self.ws_m[j],
                              prof=None if prof is None else prof[2:])
 
     def distinct_experts(self, steps):
         return (self.big["n_active"][:steps, 0] - 1).cpu().numpy()
+
+
+def capture_steps(torch, st, K, NF=1):
+    """One HIP graph of steps 0 .. K-1 of st: window i on stream i % NF (one stream: the
+    windows run one after the other), every launch of the window's kernels in it."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    side = [torch.cuda.Stream() for _ in range(NF - 1)]
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for t in side:
+                t.wait_stream(s)
+            lanes = [s] + side
+            for i in range(K):
+                with torch.cuda.stream(lanes[i % NF]):
+                    st.step(i)
+            for t in side:
+                s.wait_stream(t)
+    torch.cuda.synchronize()
+    return g
 
 
 def device_layer_types(torch, sw):
@@ -359,21 +387,7 @@ def main():
 
     # ---- the timed region: one graph of K steps (window i on stream i % inflight; the
     # windows of one stream run one after the other)
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    side = [torch.cuda.Stream() for _ in range(NF - 1)]
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for t in side:
-                t.wait_stream(s)
-            lanes = [s] + side
-            for i in range(K):
-                with torch.cuda.stream(lanes[i % NF]):
-                    st.step(i)
-            for t in side:
-                s.wait_stream(t)
-    torch.cuda.synchronize()
+    g = capture_steps(torch, st, K, NF)
     g.replay()                      # warm replay
     torch.cuda.synchronize()
     # replay() runs on the current stream: the events go there too

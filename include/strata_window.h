@@ -7,7 +7,7 @@
  * the --batch-mtp paragraph), at most eight rows (same page, option table and the
  * paragraph after it; PR #1636 "What changed": the hand-off bound is kVerifyMaxT rows).
  * The router, the shared expert, every routed expert used by any row of the window and
- * the output head are read once per window for all rows that use them. A row's
+ * the output head are fetched a single time per window, whichever rows use them. A row's
  * arithmetic does not depend on which other rows share the window (same page,
  * "Exactness"), so every kernel behind this ABI computes a row the same way whether it
  * is alone or grouped with others.
@@ -140,7 +140,7 @@ typedef struct {
 /*
  * strata_window_route - router GEMV, softmax, top-k and per-expert row grouping for one
  * window (Strata docs/BATCHING.md, opening paragraph: every routed expert the rows share
- * is read once per window; the grouping lists the rows of each expert).
+ * is fetched a single time per window; the grouping lists the rows of each expert).
  *   x        [rows][hidden], x_dtype STRATA_F32 or STRATA_BF16, row-major
  *   gate_w   [n_experts][hidden] float, row-major
  *   logit_bias [n_experts] float or NULL: added to each row's logits before softmax/top-k
@@ -163,7 +163,7 @@ int strata_window_route(void* stream, const void* x, int x_dtype, int rows, int 
  *   out[r] = sum over r's entries (ascending expert id) of entry_w * y  +  y_shared
  *            (+ residual[r] when residual != NULL)
  * (Strata docs/BATCHING.md, opening paragraph: the shared expert and the routed experts
- * are read once per window for all rows that use them.)
+ * are fetched a single time per window, whichever rows use them.)
  *   x        [rows][hidden], x_dtype; residual NULL or [rows][hidden] of x_dtype
  *   gate, up: n_mat = n_experts matrices [ffn][hidden]; down: [hidden][ffn]
  *   sh_gate, sh_up, sh_down: the shared expert, n_mat = 1, same shapes and bits
@@ -195,7 +195,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
  * unit's LDS together (bf16 activations above about 7,600 hidden, float above about
  * 4,200), the call runs the routing as a kernel of its own, as strata_window_route does,
  * and the plain gate/up: the same results. (Strata docs/BATCHING.md, opening paragraph: the router, the shared expert
- * and every routed expert the rows use are read once per window for all of them.)
+ * and each routed expert the rows use are fetched a single time per window.)
  *   ws: at least strata_window_workspace(3, ...) bytes.
  * Errors: those of strata_window_route and strata_window_moe, and a workspace smaller
  * than strata_window_workspace(3, ...).
@@ -210,7 +210,7 @@ int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int 
 
 /*
  * strata_window_head - the output head of the window (Strata docs/BATCHING.md, opening
- * paragraph: the head is read once per window; docs/MULTI_GPU.md "What each card
+ * paragraph: one fetch of the head serves the whole window; docs/MULTI_GPU.md "What each card
  * holds": the last card runs it): logits[r][v] = sum_h W[v][h] * x[r][h] over an 8-bit
  * block-quantized W [vocab][hidden], then argmax[r] = the lowest v of the largest logit.
  *   logits NULL or [rows][vocab] float; argmax [rows] int32.
@@ -244,9 +244,10 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
 /*
  * strata_window_tier - routing counts of the window and the adaptive tier's swap choice
  * (Strata docs/BATCHING.md, the paragraph on batch windows counting the experts they
- * route to: every --adapt-every windows the most-routed experts outside the fast tier are
- * swapped in for the least-routed resident ones; --adapt-decay; --adapt-min-gain F, the
- * bar a swap clears: the incoming expert's count against the outgoing one's).
+ * route to, with --adapt-every, --adapt-decay and --adapt-min-gain: the windows' routing
+ * accumulates per-expert counts, and a periodic round exchanges heavily used experts
+ * outside the fast tier for lightly used resident ones, each exchange subject to a
+ * minimum ratio of the two counts).
  *   row_mask [n_experts + 1] uint8: strata_route_out.row_mask of the window (the shared
  *            expert's entry is not counted)
  *   counts   [n_experts] float, in/out: counts[e] = fmaf(counts[e], decay, number of the

@@ -11,8 +11,9 @@
  *   - docs/BATCHING.md "Several requests at once (batch slots)", opening paragraph: a
  *     window carries one row per conversation slot and reads the router, the shared
  *     expert, the head and every routed expert the rows use once for all of them.
- *   - same page, "Exactness": a batch row's arithmetic is the one of a single-token
- *     window. So the reference computes each row alone, from its definition; grouping
+ *   - same page, "Exactness": batching does not change any row's arithmetic, which is
+ *     that of a window holding the row alone. So the reference computes each row alone,
+ *     from its definition; grouping
  *     is computed separately (oracle_group) only to check the grouping the GPU builds.
  * Where the pages leave a step open, the readings taken are:
  *   affine dequant w = scale*q + min (q unsigned), symmetric 8-bit w = scale*q;
@@ -350,11 +351,11 @@ int oracle_accept(int n_slots, int mtp, const int32_t* argmax, const int32_t* pr
 
 /*
  * Expert routing counts and the adaptive tier's swap choice (Strata docs/BATCHING.md,
- * the paragraph on batch windows counting the experts they route to: every
- * --adapt-every windows the engine swaps the most-routed experts that are not in the fast
- * tier in for the least-routed resident ones; --adapt-decay applies; --adapt-min-gain F
- * (default 1.5) is the bar a swap must clear, the incoming expert's count against the
- * outgoing one's).
+ * the paragraph on batch windows counting the experts they route to, with --adapt-every,
+ * --adapt-decay and --adapt-min-gain F, whose default is 1.5): the windows' routing builds
+ * per-expert counts; a periodic round exchanges heavily used experts outside the fast tier
+ * for lightly used resident ones, and an exchange needs the incoming count to reach F
+ * times the outgoing one.
  *
  * Readings where the pages leave the step open: a window adds, for each routed expert e,
  * the number of its rows that route to e (row_mask[e]'s bits), after scaling the running

@@ -111,3 +111,28 @@ def row_rel_err(g, o):
     num = np.max(np.abs(g - o), axis=1)
     den = np.max(np.abs(o), axis=1)
     return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num)))
+
+
+# The element-wise error: |gpu - oracle| over max(|oracle|, 1e-3 * the row's max |oracle|),
+# reported beside the row metric and held to ELEM_TOL.
+ELEM_FLOOR = 1e-3
+ELEM_TOL = None
+
+
+def elem_rel_err(g, o):
+    """Max over elements of |g - o| / max(|o|, ELEM_FLOOR * max |o| of the element's row)."""
+    g = np.atleast_2d(g); o = np.atleast_2d(o)
+    floor = ELEM_FLOOR * np.max(np.abs(o), axis=1, keepdims=True)
+    den = np.maximum(np.abs(o), floor)
+    num = np.abs(g - o)
+    return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num)))
+
+
+def assert_close(g, o):
+    """Row metric within REL_TOL (and the floored element metric within ELEM_TOL when set);
+    returns both."""
+    err, eerr = row_rel_err(g, o), elem_rel_err(g, o)
+    assert err <= REL_TOL, (err, eerr)
+    if ELEM_TOL is not None:
+        assert eerr <= ELEM_TOL, (err, eerr)
+    return err, eerr

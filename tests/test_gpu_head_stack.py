@@ -49,6 +49,13 @@ def test_head_small_f32_ragged_rows():
     head_check(cfg, synth.make_window(cfg, 1), "f32")
 
 
+def test_head_f32_hidden_1920_lds_boundary():
+    """Float rows at hidden 1920: the activation image takes exactly 64 KiB of dynamic LDS,
+    which with the kernel's static LDS needs the raised limit."""
+    cfg = synth.config("small_f32", vocab=1024, hidden=1920, rows=8)
+    head_check(cfg, synth.make_window(cfg, 3), "f32 hidden 1920")
+
+
 def test_head_large_magnitudes():
     """Rows scaled by 2^20 and 2^-20 stay exact through the per-row power-of-two scaling."""
     cfg = synth.config("stack24_head", vocab=2048, rows=3)

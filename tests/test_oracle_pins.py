@@ -443,9 +443,10 @@ def test_accept_reproduces_serial_greedy_decoding(oracle_lib):
 
 
 # ------------------------------------------------------- routing counts and the tier
-# Strata docs/BATCHING.md: batch windows count the experts they route to; every
-# --adapt-every windows the most-routed experts outside the fast tier are swapped in for
-# the least-routed resident ones, each swap clearing --adapt-min-gain (default 1.5).
+# Strata docs/BATCHING.md, the paragraph on batch windows counting the experts they route
+# to (--adapt-every, --adapt-decay, --adapt-min-gain, whose default is 1.5): per-expert
+# counts accumulate over windows; a periodic round exchanges well-used experts outside
+# the fast tier for little-used resident ones while the count ratio clears the bar.
 
 def test_tier_count_matches_bruteforce_and_decay_closed_form(oracle_lib):
     rng = np.random.default_rng(3)

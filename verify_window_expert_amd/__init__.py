@@ -241,12 +241,14 @@ class RouteOut:
         n = int(self.n_active[0].item())
         off = self.offsets[:n + 1].cpu().numpy()
         e = int(off[-1])
-        return dict(topk_idx=self.topk_idx.view(self.rows, self.top_k).cpu().numpy(),
-                    topk_w=self.topk_w.view(self.rows, self.top_k).cpu().numpy(),
+        R, K = self.rows, self.top_k
+        return dict(topk_idx=self.topk_idx[:R * K].reshape(R, K).cpu().numpy(),
+                    topk_w=self.topk_w[:R * K].reshape(R, K).cpu().numpy(),
                     n_active=n, active=self.active[:n].cpu().numpy(), offsets=off,
                     entry_row=self.entry_row[:e].cpu().numpy(), entry_w=self.entry_w[:e].cpu().numpy(),
-                    row_mask=self.row_mask.cpu().numpy(), entry_pos=self.entry_pos[:e].cpu().numpy(),
-                    row_w=self.row_w.view(self.rows, self.top_k + 1).cpu().numpy())
+                    row_mask=self.row_mask[:self.n_experts + 1].cpu().numpy(),
+                    entry_pos=self.entry_pos[:e].cpu().numpy(),
+                    row_w=self.row_w[:R * (K + 1)].reshape(R, K + 1).cpu().numpy())
 
 
 def workspace_bytes(which, rows, hidden, ffn=0, n_experts=0, top_k=0, vocab=0):

@@ -18,9 +18,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose=False):
+def build(verbose=False, defines=(), out=None):
     """Compile every HIP source of the library into libstrata_window.so (always rebuilds):
-    one hipcc per source, run side by side, then one link."""
+    one hipcc per source, run side by side, then one link. defines: extra -D options (a
+    tuning variant); out: the library's path (default: the package's)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,7 +30,8 @@ def build(verbose=False):
     for src in sources():
         obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmds.append([hipcc] + [f for f in HIPCC_FLAGS if f != "-shared"] + ["-c", src, "-o", obj])
+        cmds.append([hipcc] + [f for f in HIPCC_FLAGS if f != "-shared"] + ["-D" + d for d in defines] +
+                    ["-c", src, "-o", obj])
 
     def run(cmd):
         return subprocess.run(cmd, capture_output=True, text=True)
@@ -39,7 +41,8 @@ def build(verbose=False):
     for cmd, res in zip(cmds, results):
         if res.returncode != 0:
             raise RuntimeError("hipcc failed: " + " ".join(cmd) + "\n" + res.stdout + res.stderr)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    lib_path = out or LIB_PATH
+    tmp = lib_path + ".tmp%d" % os.getpid()
     link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     res = run(link)
     if res.returncode != 0:
@@ -49,5 +52,5 @@ def build(verbose=False):
     for o in objs:
         os.remove(o)
     os.rmdir(tmpdir)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path

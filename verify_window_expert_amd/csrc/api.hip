@@ -42,8 +42,8 @@ struct MoeWs { size_t h, y, total; };
 MoeWs moe_ws(int rows, int hidden, int ffn, int top_k) {
   const size_t ent = (size_t)rows * top_k + rows;
   MoeWs w;
-  w.h = STRATA_WS_COUNTER_BYTES;                          // bf16 hi + lo per entry and input
-  w.y = round_up(w.h + 4 * ent * ffn, 256);
+  w.h = STRATA_WS_COUNTER_BYTES;                          // bf16 hi, then bf16 lo, per entry and input
+  w.y = round_up(w.h + 4 * ent * ffn, 256);               // the experts' outputs per entry
   w.total = round_up(w.y + 4 * ent * hidden, 256);
   return w;
 }
@@ -252,15 +252,16 @@ int prepare_moe(const void* x, int x_dtype, int rows, int hidden, int ffn, const
   g.n_active = route->n_active; g.active = route->active; g.offsets = route->offsets; g.entry_row = route->entry_row;
   g.row_mask = route->row_mask;
   g.max_slots = max_slots;
-  g.h_img = (uint32_t*)((char*)ws + w.h);
+  const int n_ent = rows * top_k + rows;
+  g.h_hi = (uint16_t*)((char*)ws + w.h);
+  g.h_lo = g.h_hi + (size_t)n_ent * ffn;
 
   d.x_res = residual; d.x_dtype = x_dtype; d.rows = rows; d.hidden = hidden; d.ffn = ffn; d.bits = bits;
   d.n_experts = n_experts;
   d.down = qdev(down, sh_down);
   d.n_active = route->n_active; d.active = route->active; d.offsets = route->offsets;
-  d.entry_row = route->entry_row; d.entry_w = route->entry_w; d.row_mask = route->row_mask;
-  d.entry_pos = route->entry_pos; d.row_w = route->row_w;
-  d.h_img = g.h_img; d.y = (float*)((char*)ws + w.y); d.out = out; d.x_next = x_next_bf16;
+  d.entry_row = route->entry_row; d.entry_pos = route->entry_pos; d.row_w = route->row_w;
+  d.h_hi = g.h_hi; d.h_lo = g.h_lo; d.h_entries = n_ent; d.y = (float*)((char*)ws + w.y); d.out = out; d.x_next = x_next_bf16;
   d.max_slots = max_slots; d.top_k = top_k;
   return STRATA_OK;
 }
@@ -301,7 +302,7 @@ int strata_window_moe(void* stream, const void* x, int x_dtype, int rows, int hi
   const sw::Prof pg = prof(prof_events, 0), pd = prof(prof_events, 2);
   int rc;
   if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
-  return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
+  return launch_status(sw::launch_down(d, s, prof_events ? &pd : nullptr), "down");
 }
 
 int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
@@ -337,7 +338,7 @@ int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int 
     if ((rc = launch_status(sw::launch_route(r, s, prof_events ? &pr : nullptr), "router"))) return rc;
     if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
   }
-  return launch_status(sw::launch_down(d, max_slots, s, prof_events ? &pd : nullptr), "down");
+  return launch_status(sw::launch_down(d, s, prof_events ? &pd : nullptr), "down");
 }
 
 int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn, int n_experts,
@@ -390,7 +391,8 @@ int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int 
     if (!argmax || !aligned(argmax, 16)) return fail(STRATA_EINVAL, "argmax NULL or not 16-byte aligned");
     if (logits && !aligned(logits, 16)) return fail(STRATA_EINVAL, "logits not 16-byte aligned");
     const size_t lds = (size_t)8 * (hidden + 8) * 2 + (size_t)(hidden / 32) * 64;
-    if (lds > kLdsLimit) return fail(STRATA_EUNSUPPORTED, "hidden %d needs more than %zu bytes of LDS", hidden, kLdsLimit);
+    if (lds + kStaticLds > kLdsLimit)
+      return fail(STRATA_EUNSUPPORTED, "hidden %d needs more than %zu bytes of LDS", hidden, kLdsLimit);
     ha.x = x_final; ha.x_dtype = STRATA_BF16; ha.rows = rows; ha.hidden = hidden; ha.vocab = vocab;
     ha.codes = (const uint8_t*)head->codes; ha.meta = (const uint8_t*)head->meta;
     ha.logits = logits; ha.argmax = argmax;
@@ -422,7 +424,7 @@ int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int 
     if ((rc = launch_status(fused ? sw::launch_gateup_routed(g, max_slots, s, nullptr)
                                   : sw::launch_gateup(g, max_slots, s, nullptr), "gate/up")))
       return rc;
-    if ((rc = launch_status(sw::launch_down(d, max_slots, s, last_layer && !head ? p_last : nullptr, last_layer),
+    if ((rc = launch_status(sw::launch_down(d, s, last_layer && !head ? p_last : nullptr, last_layer),
                             "down")))
       return rc;
     if (!last_layer) {
@@ -454,7 +456,8 @@ int strata_window_head(void* stream, const void* x, int x_dtype, int rows, int h
   if (!argmax || !aligned(argmax, 16)) return fail(STRATA_EINVAL, "argmax NULL or not 16-byte aligned");
   if (logits && !aligned(logits, 16)) return fail(STRATA_EINVAL, "logits not 16-byte aligned");
   const size_t lds = (size_t)(x_dtype == STRATA_F32 ? 16 : 8) * (hidden + 8) * 2 + (size_t)(hidden / 32) * 64;
-  if (lds > kLdsLimit) return fail(STRATA_EUNSUPPORTED, "hidden %d needs more than %zu bytes of LDS", hidden, kLdsLimit);
+  if (lds + kStaticLds > kLdsLimit)
+    return fail(STRATA_EUNSUPPORTED, "hidden %d needs more than %zu bytes of LDS", hidden, kLdsLimit);
   const HeadWs w = head_ws(rows, vocab);
   if (ws_bytes < w.total) return fail(STRATA_EINVAL, "head workspace %zu < %zu bytes", ws_bytes, w.total);
 

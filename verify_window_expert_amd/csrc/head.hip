@@ -1,7 +1,7 @@
 // Output head of a verify window: 8-bit block-quantized GEMV and per-row argmax.
 //
 // Strata docs/BATCHING.md, "Several requests at once (batch slots)", opening paragraph:
-// the head is read once per window for all its rows; docs/MULTI_GPU.md, "What each card
+// a single fetch of the head serves every row of the window; docs/MULTI_GPU.md, "What each card
 // holds": it runs on the card that holds the last layers.
 //
 // Matrix-core formulation, as for the experts but in binary16: a lane's 8 signed codes
@@ -12,7 +12,6 @@
 //     sum_k w x = scale * (D - 1152 * Sx),  D = sum (1152 + q) x.
 // A second one-workgroup launch reduces the per-workgroup argmax candidates.
 #include <algorithm>
-#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -92,7 +91,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(HeadArgs a) {
   auto issue = [&](auto d_) __attribute__((always_inline)) {
     constexpr int d = decltype(d_)::value;
     const long chunk = (long)(gw + is_j * TW) * NG + is_g;
-    // read once per window: non-temporal loads (measured faster than plain ones here)
+    // each weight is used by one window only: non-temporal loads (measured faster here)
     rc[d] = __builtin_nontemporal_load(codes + chunk * 64 + lane);
     rm[d] = __builtin_nontemporal_load(meta + chunk * 16 + c);
     if (++is_g == NG) {
@@ -312,15 +311,7 @@ int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p) {
 
 template <bool F32IN, int XG>
 static int launch_head_k(const HeadArgs& a, size_t lds, int nwg, hipStream_t s, const Prof* p) {
-  static std::mutex m;
-  static size_t granted = 64 * 1024;   // raise the dynamic LDS limit once, when needed
-  std::lock_guard<std::mutex> lock(m);
-  if (lds > granted) {
-    if (int e = (int)hipFuncSetAttribute((const void*)k_head<F32IN, XG>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)lds))
-      return e;
-    granted = lds;
-  }
+  if (int e = set_lds<k_head<F32IN, XG>>(lds)) return e;
   launch(k_head<F32IN, XG>, dim3(nwg), dim3(kHeadThreads), lds, s, p, a);
   return 0;
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace sw {
 
 struct RouteArgs {
@@ -28,7 +30,8 @@ struct GateUpArgs {
   QDev gate, up;
   const int32_t* n_active; const int32_t* active; const int32_t* offsets;
   const int32_t* entry_row; const uint8_t* row_mask;
-  uint32_t* h_img;          // [entries][ffn]: h as bf16 hi | lo << 16, in the permuted order
+  uint16_t* h_hi;           // [entries][ffn]: h rounded to bf16, in the permuted order
+  uint16_t* h_lo;           // [entries][ffn]: bf16 rounding of h - hi, same order
   int max_slots;            // capacity of the active array (offsets: max_slots + 1)
   int split;                // set by the launcher: waves per item (1 or 2), fixed by the
                             // shapes alone so a row's sums never depend on the window
@@ -38,12 +41,11 @@ struct DownArgs {
   const void* x_res; int x_dtype; int rows, hidden, ffn, bits, n_experts;
   QDev down;
   const int32_t* n_active; const int32_t* active; const int32_t* offsets;
-  const int32_t* entry_row; const float* entry_w; const uint8_t* row_mask;
-  const int32_t* entry_pos; const float* row_w;
-  const uint32_t* h_img;    // as GateUpArgs
+  const int32_t* entry_row; const int32_t* entry_pos; const float* row_w;
+  const uint16_t* h_hi; const uint16_t* h_lo;   // as GateUpArgs
+  int h_entries;            // entries the h arrays hold (rows * top_k + rows)
   float* y;                 // [rows][top_k + 1][hidden]: row r's experts in ascending id order
-  float* out; uint16_t* x_next;   // out may be NULL (a stack layer whose float output nobody reads)
-  int n_ranges;             // 64-row output ranges
+  float* out; uint16_t* x_next;   // either may be NULL
   int max_slots, top_k;     // capacity of the active / offsets arrays; routing top-k
 };
 
@@ -100,6 +102,24 @@ inline void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, c
     hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
 }
 
+// Raise a kernel's dynamic LDS limit when its static LDS plus `bytes` of dynamic LDS
+// exceed the default 64 KB (once per process and kernel; the attribute only grows).
+template <auto kernel>
+inline int set_lds(size_t bytes) {
+  static std::mutex m;
+  static size_t granted = 0;
+  std::lock_guard<std::mutex> lock(m);
+  if (bytes <= granted) return 0;
+  hipFuncAttributes fa;
+  if (int e = (int)hipFuncGetAttributes(&fa, (const void*)kernel)) return e;
+  if (fa.sharedSizeBytes + bytes > 64 * 1024) {
+    const int e = (int)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e) return e;
+  }
+  granted = bytes;
+  return 0;
+}
+
 // Launchers return the hipError_t of the launch (0 on success).
 int launch_route(const RouteArgs& a, hipStream_t s, const Prof* p);
 int launch_gateup(const GateUpArgs& a, int max_slots, hipStream_t s, const Prof* p);
@@ -111,18 +131,18 @@ int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, cons
 int launch_route_logits(const RouteArgs& a, hipStream_t s, const Prof* p);
 int launch_route_final(const RouteArgs& a, hipStream_t s, const Prof* p);
 // down, then (combine) the combine kernel
-int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p, bool combine = true);
-// layer l's combine and layer l + 1's router GEMV in one launch (res_f32: layer l's input is float)
+int launch_down(const DownArgs& a, hipStream_t s, const Prof* p, bool combine = true);
+// layer l's combine and layer l + 1's router GEMV in one launch (res_f32: layer l's input
+// is float)
 int launch_combine_route(const CombineRouteArgs& c, int res_f32, hipStream_t s, const Prof* p);
+size_t down_lds_bytes(int ffn);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
 int launch_tier(const TierArgs& a, hipStream_t s, const Prof* p);
 int launch_stream_read(const StreamArgs& a, hipStream_t s, const Prof* p);
 int head_workgroups(int vocab);
-int down_ranges(int hidden);
-// dynamic LDS of the gate/up and down kernels (the activation image)
+// dynamic LDS of the gate/up kernel (the activation image)
 size_t gateup_lds_bytes(int hidden, int x_dtype);
 size_t route_core_lds_bytes();   // the fused layer's gate/up: the routing core's static LDS
-size_t down_lds_bytes(int ffn);
 
 }  // namespace sw

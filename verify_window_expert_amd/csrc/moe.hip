@@ -2,9 +2,9 @@
 // matvec with the weighted combine of each row's experts and the shared expert.
 //
 // Strata docs/BATCHING.md, "Several requests at once (batch slots)", opening paragraph:
-// the shared expert and every routed expert the rows use are read once per window for
-// all of them; "Exactness": a row's arithmetic must not depend on how many rows share
-// an expert, so every expert runs the same code for any number of rows.
+// a window fetches the shared expert and each routed expert its rows use a single time,
+// whichever rows share them; "Exactness": a row's arithmetic must not depend on how many
+// rows share an expert, so every expert runs the same code for any number of rows.
 //
 // Matrix-core formulation. The window's rows (at most 8) are the 16-wide M side of a
 // v_mfma_f32_16x16x32_bf16: columns 0..7 hold the rows' activations rounded to bf16
@@ -40,7 +40,7 @@ constexpr int kGuDepth = SW_GU_DEPTH;                // gate/up: units in flight
 #endif
 constexpr int kDnDepth = SW_DN_DEPTH;                // down: units in flight per wave
 #ifndef SW_WEIGHT_AUX
-#define SW_WEIGHT_AUX 2                              // weight loads: non-temporal (read once per window;
+#define SW_WEIGHT_AUX 2                              // weight loads: non-temporal (one use per window;
 #endif                                               // measured faster than plain loads)
 
 // ------------------------------------------------------------ activation operand (LDS)
@@ -69,7 +69,6 @@ __host__ __device__ inline size_t act_lds_bytes(int K, int nrows) {
 }
 
 size_t gateup_lds_bytes(int hidden, int x_dtype) { return act_lds_bytes(hidden, x_dtype == 0 ? 16 : 8); }
-size_t down_lds_bytes(int ffn) { return act_lds_bytes(ffn, 16); }
 
 // Convert 8 consecutive source values of row j (inputs 8u..8u+7) to bf16 hi (and lo),
 // store them permuted, and add the block sums (4 consecutive lanes = one block).
@@ -176,36 +175,6 @@ __device__ __forceinline__ void stage_group_bf16(const ActLds& l, bool ok, int j
   if (ok) {
     *(u32x4*)(l.xs + (size_t)j * l.stride + 8 * u) = ph;
     if ((u & 3) == 0) l.sx[(u >> 2) * 16 + j] = shi;
-  }
-}
-
-// A group of 8 inputs already split into bf16 hi | lo << 16 words in the image order
-// (the down kernel's h): byte permutes give the hi and lo words, and the block sums add
-// the group's values in image order, then over the 4 lanes of the block.
-__device__ __forceinline__ void stage_group_hl(const ActLds& l, bool ok, int j, int u, const u32x4 (&w)[2]) {
-  u32x4 ph, pl;
-#pragma unroll
-  for (int t = 0; t < 4; t++) {
-    const uint32_t w0 = w[t >> 1][2 * (t & 1)], w1 = w[t >> 1][2 * (t & 1) + 1];
-    ph[t] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-    pl[t] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-  }
-  float shi = 0.f, slo = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; e++) {
-    const uint32_t word = w[e >> 2][e & 3];
-    shi += __uint_as_float(word << 16);
-    slo += __uint_as_float(word & 0xFFFF0000u);
-  }
-  shi = quad_sum(shi);
-  slo = quad_sum(slo);
-  if (ok) {
-    *(u32x4*)(l.xs + (size_t)j * l.stride + 8 * u) = ph;
-    *(u32x4*)(l.xs + (size_t)(8 + j) * l.stride + 8 * u) = pl;
-    if ((u & 3) == 0) {
-      l.sx[(u >> 2) * 16 + j] = shi;
-      l.sx[(u >> 2) * 16 + 8 + j] = slo;
-    }
   }
 }
 
@@ -539,7 +508,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
         const float hv = gv / (1.f + expf(-gv)) * us[i];
         const uint32_t hi = f32_to_bf16(hv);
         const uint32_t lo = f32_to_bf16(hv - bf16_to_f32((uint16_t)hi));
-        a.h_img[(long)ent * F + tile * 16 + f_pos] = hi | (lo << 16);
+        a.h_hi[(long)ent * F + tile * 16 + f_pos] = (uint16_t)hi;
+        a.h_lo[(long)ent * F + tile * 16 + f_pos] = (uint16_t)lo;
       }
     }
   };
@@ -606,17 +576,54 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   });
 }
 
-// --------------------------------------------------------------------------- down
-// Persistent, 16-wave workgroups (so that each (slot, output tile) item gets a wave of
-// its own at the usual shapes); workgroup b serves expert slot b % n_active (the
+// ----------------------------------------------------------------------------- down
+// Down, then the combine. A k_down workgroup serves one expert slot (the workgroups of a
+// slot split its output tiles) and stages that expert's h once; y is written per entry at
+// its place in its row's ascending list of experts, and k_combine adds each row's list in
+// order (routed experts ascending, the shared expert last, with combine_one), then the
+// residual. In the stack, k_combine_route (route.hip) takes the combine's place between
+// layers. Every sum is a function of the row's own values, so a row is the same in any
+// window.
+//
+// h comes from gate/up as two bf16 arrays (hi, and the rounding of the remainder lo),
+// [entries][ffn], inputs permuted within each group of 8 as the code conversion orders
+// them; the block sums Sx the min term needs are formed while staging, in LDS.
+
+
+// k_down: persistent, 16-wave workgroups (so that each (slot, output tile) item gets a
+// wave of its own at the usual shapes); workgroup b serves expert slot b % n_active (the
 // workgroups of a slot split its output tiles) and stages that expert's h once; each
 // wave streams whole 16-row output tiles through the ring. y is written for each of the
 // expert's rows at that row's place in its ascending list of experts; k_combine sums
-// each row's list in order. As in gate/up, h (from L2) is staged
-// in LDS before the weights are requested.
+// each row's list in order. As in gate/up, h (from L2) is staged in LDS while the first
+// weights are in flight.
 
 constexpr int kDnWaves = 16, kDnThreads = 64 * kDnWaves;
-constexpr int kDownRange = 64;   // rows per combine workgroup
+size_t down_lds_bytes(int ffn) { return act_lds_bytes(ffn, 16); }
+
+// 8 inputs of row j already split into bf16 hi and lo in the image order: stored as
+// they are, and the block sums add the group's values in image order, then over the 4
+// lanes of the block (the layout of ActLds: hi rows 0..7, lo rows 8..15).
+__device__ __forceinline__ void stage_group_split(const ActLds& l, bool ok, int j, int u, const u32x4& wh,
+                                                  const u32x4& wl) {
+  float shi = 0.f, slo = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const uint32_t h = wh[e >> 1], lo = wl[e >> 1];
+    shi += __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16));
+    slo += __uint_as_float((e & 1) ? (lo & 0xFFFF0000u) : (lo << 16));
+  }
+  shi = quad_sum(shi);
+  slo = quad_sum(slo);
+  if (ok) {
+    *(u32x4*)(l.xs + (size_t)j * l.stride + 8 * u) = wh;
+    *(u32x4*)(l.xs + (size_t)(8 + j) * l.stride + 8 * u) = wl;
+    if ((u & 3) == 0) {
+      l.sx[(u >> 2) * 16 + j] = shi;
+      l.sx[(u >> 2) * 16 + 8 + j] = slo;
+    }
+  }
+}
 
 template <int BITS, int XG>
 __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
@@ -650,20 +657,18 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   const int my_tiles = t0 < tiles_h ? (tiles_h - t0 + stride - 1) / stride : 0;
   const int units = my_tiles * NG;
 
-  // the expert's h as the gate/up kernel wrote it (XG groups of 8 inputs per thread, two
-  // 16-byte words each: group i is row i / (F/8), inputs 8 (i % (F/8)) ..), and where
-  // each of its entries' y goes: row r's list of experts in ascending id order, position
-  // entry_pos
+  // the expert's h as gate/up wrote it (XG groups of 8 inputs per thread, hi and lo:
+  // group i is row i / (F/8), inputs 8 (i % (F/8)) ..), and where each of its entries' y
+  // goes: row r's list of experts in ascending id order, position entry_pos
   const ActLds l = act_lds(smem, F, 16);
   const int ngrp = F / 8, total = max(ne, 1) * ngrp;
-  const uint32_t* hsrc = a.h_img + (long)e0 * F;
   u32x4 hr[XG][2];
 #pragma unroll
   for (int it = 0; it < XG; it++) {
     const int i = min(it * kDnThreads + tid, total - 1);
-    const u32x4* p = (const u32x4*)(hsrc + (long)(i / ngrp) * F + 8 * (i % ngrp));
-    hr[it][0] = p[0];
-    hr[it][1] = p[1];
+    const long at = (long)(e0 + i / ngrp) * F + 8 * (i % ngrp);
+    hr[it][0] = *(const u32x4*)(a.h_hi + at);
+    hr[it][1] = *(const u32x4*)(a.h_lo + at);
   }
   const int ej = e0 + min(lane, max(ne, 1) - 1);
   const int dst_row = a.entry_row[ej], dst_pos = a.entry_pos[ej];
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
       const int base = it * kDnThreads;
       if (base >= total_e) break;
       const int i = base + tid;
-      stage_group_hl(l, i < total_e, i < total_e ? i / ngrp : 0, i < total_e ? i % ngrp : 0, hr[it]);
+      stage_group_split(l, i < total_e, i < total_e ? i / ngrp : 0, i < total_e ? i % ngrp : 0, hr[it][0], hr[it][1]);
     }
   };
   if (units == 0) {
@@ -825,24 +830,6 @@ static int persistent_grid(int threads, size_t lds, int max_items, int per_cu_ma
   return max_items < resident ? max_items : resident;
 }
 
-// Raise a kernel's dynamic LDS limit when static + dynamic exceed the default 64 KB (once
-// per process and kernel; the attribute only grows).
-template <auto kernel>
-static int set_lds(size_t bytes) {
-  static std::mutex m;
-  static size_t granted = 0;
-  std::lock_guard<std::mutex> lock(m);
-  if (bytes <= granted) return 0;
-  hipFuncAttributes fa;
-  if (int e = (int)hipFuncGetAttributes(&fa, (const void*)kernel)) return e;
-  if (fa.sharedSizeBytes + bytes > 64 * 1024) {
-    const int e = (int)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e) return e;
-  }
-  granted = bytes;
-  return 0;
-}
-
 template <int BITS, bool F32IN, int XG, bool ROUTED>
 static int launch_gateup_k(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
   auto kern = k_gateup<BITS, F32IN, XG, ROUTED>;
@@ -896,8 +883,6 @@ int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, cons
   return launch_gateup_any<true>(a, max_slots, s, p);
 }
 
-int down_ranges(int hidden) { return (hidden + kDownRange - 1) / kDownRange; }
-
 template <int BITS, int XG>
 static int launch_down_k(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
   if (int e = set_lds<k_down<BITS, XG>>(lds)) return e;
@@ -917,13 +902,13 @@ static int launch_down_bits(const DownArgs& a, size_t lds, int max_slots, hipStr
   return (int)hipErrorInvalidValue;
 }
 
-int launch_down(const DownArgs& a, int max_slots, hipStream_t s, const Prof* p, bool combine) {
+int launch_down(const DownArgs& a, hipStream_t s, const Prof* p, bool combine) {
   const size_t lds = down_lds_bytes(a.ffn);
   Prof p0, p1;
   if (p) { p0.start = p->start; p1.stop = p->stop; }
   if (!combine) p0.stop = p1.stop;
-  const int e = a.bits == 4 ? launch_down_bits<4>(a, lds, max_slots, s, p ? &p0 : nullptr)
-                            : launch_down_bits<2>(a, lds, max_slots, s, p ? &p0 : nullptr);
+  const int e = a.bits == 4 ? launch_down_bits<4>(a, lds, a.max_slots, s, p ? &p0 : nullptr)
+                            : launch_down_bits<2>(a, lds, a.max_slots, s, p ? &p0 : nullptr);
   if (e || !combine) return e;
   const int cg = (a.rows * (a.hidden / kCombineVec) + kCombineThreads - 1) / kCombineThreads;
   if (a.x_dtype == 0)

@@ -2,7 +2,7 @@
 // the lower expert index winning ties, and the per-expert row lists of the window.
 //
 // Strata docs/BATCHING.md, "Several requests at once (batch slots)", opening paragraph:
-// the router and every routed expert the window's rows use are read once for all of
+// the router and each routed expert the window's rows use are fetched a single time for all of
 // them; the row lists built here are what lets the expert kernels do that.
 //
 // Two launches. k_route_logits: workgroup (row group, expert group, input chunk), each of
@@ -247,9 +247,10 @@ __global__ __launch_bounds__(kRouteCoreThreads) void k_route_final(RouteArgs a) 
 
 // ---------------------------------------------------------- routing counts and tier
 // Strata docs/BATCHING.md, the paragraph on batch windows counting the experts they route
-// to: every --adapt-every windows the most-routed experts outside the fast tier are
-// swapped in for the least-routed resident ones, each swap clearing --adapt-min-gain (the
-// incoming count against the outgoing one). One workgroup, thread e = expert e:
+// to (--adapt-every, --adapt-decay, --adapt-min-gain): each window's routing adds to a
+// per-expert count; on a selection round, experts outside the fast tier with high counts
+// replace resident experts with low counts, a pair at a time, while the incoming count
+// clears min_gain times the outgoing one. One workgroup, thread e = expert e:
 //   counts[e] = fmaf(counts[e], decay, rows of the window routed to e)   (float)
 // and, on a selection round, each expert's rank in its list (outside the tier: count
 // descending; resident: ascending; ties to the lower index), then pair i = (i-th

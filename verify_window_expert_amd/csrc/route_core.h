@@ -4,8 +4,8 @@
 // expert last, their rows, and each entry's place in its row's list).
 //
 // Strata docs/BATCHING.md, "Several requests at once (batch slots)", opening paragraph:
-// the routed experts the window's rows use are read once for all of them; the row lists
-// built here are what lets the expert kernels do that.
+// each routed expert is fetched a single time per window, however many rows use it; the
+// row lists built here are what lets the expert kernels do that.
 #pragma once
 #include "common.h"
 #include "kernels.h"
