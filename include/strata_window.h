@@ -209,6 +209,30 @@ int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int 
                         uint16_t* x_next_bf16, void* ws, size_t ws_bytes, void* const* prof_events);
 
 /*
+ * strata_window_layer_noalloc - strata_window_layer without a workspace argument, for
+ * callers that cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, and harnesses that forbid allocation. The call itself allocates nothing;
+ * its workspace is a fixed array of STRATA_NOALLOC_SCRATCH_BYTES in the library's device
+ * memory, one per GPU, held until the process ends (the first call on a device looks up
+ * that device's copy). The caller still provides every input and output, as for
+ * strata_window_layer, whose arguments, results and errors this call has.
+ *   Every call on one GPU uses that GPU's array: calls that may overlap in time on the
+ *   same GPU (two streams, two host threads) race on it and must not be made. The array
+ *   needs no initialisation and keeps whatever the last call left there.
+ * Errors: those of strata_window_layer; STRATA_EINVAL when the shape's workspace
+ * (strata_window_workspace(3, ...)) exceeds STRATA_NOALLOC_SCRATCH_BYTES (nothing is
+ * enqueued); STRATA_EHIP when the array's address cannot be looked up.
+ */
+#define STRATA_NOALLOC_SCRATCH_BYTES (2u << 20)
+int strata_window_layer_noalloc(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
+                                const float* gate_w, const float* logit_bias, int flags,
+                                const strata_qmat* gate, const strata_qmat* up, const strata_qmat* down,
+                                const strata_qmat* sh_gate, const strata_qmat* sh_up,
+                                const strata_qmat* sh_down, int n_experts, int top_k,
+                                const strata_route_out* route, const void* residual, float* out,
+                                uint16_t* x_next_bf16, void* const* prof_events);
+
+/*
  * strata_window_head - the output head of the window (Strata docs/BATCHING.md, opening
  * paragraph: one fetch of the head serves the whole window; docs/MULTI_GPU.md "What each card
  * holds": the last card runs it): logits[r][v] = sum_h W[v][h] * x[r][h] over an 8-bit

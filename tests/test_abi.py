@@ -257,3 +257,23 @@ def test_stack_rejects_and_workspace(sw):
     w4h = sw.workspace_bytes(4, 8, 2048, 768, 128, 8, 151936)
     assert w4 >= w3 + 2 * 2 * 8 * 2048
     assert w4h >= w4 + sw.workspace_bytes(2, 8, 2048, vocab=151936) - 4096
+
+
+def test_noalloc_rejects_before_any_device_call(sw):
+    """strata_window_layer_noalloc refuses a shape whose workspace exceeds its fixed scratch
+    array, and an out-of-range shape, before it looks at the device (no GPU here)."""
+    L = sw.library()
+    assert L.strata_window_workspace(3, 8, 7936, 4096, 256, 8, 0) > sw.NOALLOC_SCRATCH_BYTES
+    assert L.strata_window_workspace(3, 8, 2048, 768, 128, 8, 0) <= sw.NOALLOC_SCRATCH_BYTES
+
+    def call(rows, hidden, ffn, E, k):
+        qs = [qm(sw, ffn, hidden, 4, E), qm(sw, ffn, hidden, 4, E), qm(sw, hidden, ffn, 4, E),
+              qm(sw, ffn, hidden, 4, 1), qm(sw, ffn, hidden, 4, 1), qm(sw, hidden, ffn, 4, 1)]
+        ro = route_out(sw)
+        return L.strata_window_layer_noalloc(None, A, 1, rows, hidden, ffn, A, None, 0,
+                                             *[ctypes.byref(q) for q in qs], E, k, ctypes.byref(ro), None, A, None,
+                                             None)
+    assert call(8, 7936, 4096, 256, 8) == sw.STRATA_EINVAL
+    assert b"scratch" in L.strata_window_last_error()
+    assert call(9, 2048, 768, 128, 8) == sw.STRATA_EINVAL
+    assert call(8, 2048, 768, 128, 0) == sw.STRATA_EINVAL

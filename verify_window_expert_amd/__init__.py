@@ -16,6 +16,7 @@ STRATA_OK, STRATA_EINVAL, STRATA_EUNSUPPORTED, STRATA_EHIP = 0, -1, -2, -3
 STRATA_F32, STRATA_BF16 = 0, 1
 STRATA_ROUTE_RENORM = 1
 MAX_ROWS, MAX_TOPK, MAX_EXPERTS = 8, 8, 256
+NOALLOC_SCRATCH_BYTES = 2 << 20
 WS_COUNTER_BYTES = 4096
 
 
@@ -64,6 +65,9 @@ def library():
         L.strata_window_layer.argtypes = [P, P, I, I, I, I, P, P, I] + [ctypes.POINTER(CQMat)] * 6 + \
             [I, I, ctypes.POINTER(CRouteOut), P, P, P, P, S, P]
         L.strata_window_layer.restype = I
+        L.strata_window_layer_noalloc.argtypes = [P, P, I, I, I, I, P, P, I] + [ctypes.POINTER(CQMat)] * 6 + \
+            [I, I, ctypes.POINTER(CRouteOut), P, P, P, P]
+        L.strata_window_layer_noalloc.restype = I
         L.strata_window_accept.argtypes = [P, P, I, I, I, P, P, P, P, P]
         L.strata_window_accept.restype = I
         L.strata_window_tier.argtypes = [P, P, I, P, ctypes.c_float, P, I, ctypes.c_float, P, P, P]
@@ -318,6 +322,26 @@ def strata_window_layer(x, gate_w, bias, top_k, gate, up, down, sh_gate, sh_up, 
                                          *[ctypes.byref(q) for q in qs], E, top_k, ctypes.byref(ro),
                                          _ptr(residual), _ptr(out), _ptr(x_next), _ptr(ws), _ws_bytes(ws),
                                          _events(prof)))
+    return out, route
+
+
+def strata_window_layer_noalloc(x, gate_w, bias, top_k, gate, up, down, sh_gate, sh_up, sh_down, renorm=False,
+                                route=None, residual=None, out=None, x_next=None, stream=None, prof=None):
+    """strata_window_layer with the library's fixed per-GPU scratch array as its workspace
+    (the C call allocates nothing; pass route and out to allocate nothing here either).
+    Returns (out, route) as strata_window_layer."""
+    rows, hidden = _need_x(x)
+    E = _need_router(gate_w, bias, hidden)
+    route = RouteOut(rows, E, top_k, x.device) if route is None else _need_route(route, rows, E, top_k)
+    _need_outs(x, rows, hidden, residual, out, x_next)
+    if out is None:
+        out = torch.empty(rows, hidden, dtype=torch.float32, device=x.device)
+    qs = [q.c() for q in (gate, up, down, sh_gate, sh_up, sh_down)]
+    ro = route.c()
+    _check(library().strata_window_layer_noalloc(_stream(stream), _ptr(x), _x_dtype(x), rows, hidden, gate.rows,
+                                                 _ptr(gate_w), _ptr(bias), STRATA_ROUTE_RENORM if renorm else 0,
+                                                 *[ctypes.byref(q) for q in qs], E, top_k, ctypes.byref(ro),
+                                                 _ptr(residual), _ptr(out), _ptr(x_next), _events(prof)))
     return out, route
 
 

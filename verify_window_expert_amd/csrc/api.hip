@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/strata_window.h"
 #include "kernels.h"
@@ -164,6 +165,38 @@ sw::QDev qdev(const strata_qmat* routed, const strata_qmat* shared) {
   d.sh_codes = (const uint8_t*)shared->codes;
   d.sh_meta = (const uint8_t*)shared->meta;
   return d;
+}
+
+// ------------------------------------------------- fixed scratch of the no-allocation call
+// strata_window_layer_noalloc's workspace: a file-scope device array, of which every GPU
+// holds its own copy. In host code `scratch` is only a stand-in for the symbol: its device
+// address is looked up once per device (with that device current) and kept; only that
+// address is ever passed to a kernel.
+constexpr size_t kScratchBytes = (size_t)STRATA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The current device's scratch address, or NULL with *rc set.
+void* scratch_ptr(int* rc) {
+  static std::mutex m;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  const hipError_t ed = hipGetDevice(&dev);
+  if (ed != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = fail(STRATA_EHIP, "no current device for the scratch array (%s)", hipGetErrorString(ed));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(m);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *rc = fail(STRATA_EHIP, "scratch array address on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
 }
 
 }  // namespace
@@ -339,6 +372,28 @@ int strata_window_layer(void* stream, const void* x, int x_dtype, int rows, int 
     if ((rc = launch_status(sw::launch_gateup(g, max_slots, s, prof_events ? &pg : nullptr), "gate/up"))) return rc;
   }
   return launch_status(sw::launch_down(d, s, prof_events ? &pd : nullptr), "down");
+}
+
+int strata_window_layer_noalloc(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn,
+                                const float* gate_w, const float* logit_bias, int flags, const strata_qmat* gate,
+                                const strata_qmat* up, const strata_qmat* down, const strata_qmat* sh_gate,
+                                const strata_qmat* sh_up, const strata_qmat* sh_down, int n_experts, int top_k,
+                                const strata_route_out* route, const void* residual, float* out,
+                                uint16_t* x_next_bf16, void* const* prof_events) {
+  g_err[0] = 0;
+  // the shape's workspace must fit the fixed array (checked before any device call)
+  const size_t need = strata_window_workspace(3, rows, hidden, ffn, n_experts, top_k, 0);
+  if (need == 0)
+    return fail(STRATA_EINVAL, "rows %d / hidden %d / ffn %d / n_experts %d / top_k %d out of range", rows, hidden,
+                ffn, n_experts, top_k);
+  if (need > kScratchBytes)
+    return fail(STRATA_EINVAL, "this shape needs %zu bytes of scratch, more than the fixed %zu", need, kScratchBytes);
+  int rc = STRATA_OK;
+  void* ws = scratch_ptr(&rc);
+  if (!ws) return rc;
+  return strata_window_layer(stream, x, x_dtype, rows, hidden, ffn, gate_w, logit_bias, flags, gate, up, down,
+                             sh_gate, sh_up, sh_down, n_experts, top_k, route, residual, out, x_next_bf16, ws,
+                             kScratchBytes, prof_events);
 }
 
 int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int hidden, int ffn, int n_experts,
