@@ -376,6 +376,53 @@ def cpu_baseline(cfg, host_layer, seconds, threads=None):
                       f"experts, {dt:.1f} s wall clock, OpenMP threads = {used}"}
 
 
+def cpu_baseline_stack(cfg, seconds, threads=None):
+    """The CPU oracle on the stack workload, sampled: whole layers of the stack (window 0's
+    rows through layers 0, 1, ... with the residual, each layer's input the previous one's
+    x_next) until about 3/4 of `seconds` pass, then the head on a slice of the vocabulary
+    for the rest; one window's time = 24 x the mean layer time + the head time scaled to
+    the whole vocabulary."""
+    import oracle
+    import synth
+    oracle.build(force=False)
+    all_threads = oracle.threads()
+    if threads:
+        oracle.set_threads(threads)
+    H, F, E, b, K = cfg.hidden, cfg.ffn, cfg.experts, cfg.bits, cfg.top_k
+    q = lambda m, n, r, c: oracle.qmat(m[0], m[1], r, c, b, n)
+    x = synth.make_window(cfg, 0)
+    n, t_layers, t0 = 0, 0.0, time.time()
+    while n < cfg.layers:
+        L = synth.make_layer(cfg, n)
+        mats = (q(L.gate, E, F, H), q(L.up, E, F, H), q(L.down, E, H, F),
+                q(L.sh_gate, 1, F, H), q(L.sh_up, 1, F, H), q(L.sh_down, 1, H, F))
+        t1 = time.time()
+        _, _, idx, w = oracle.route(x, L.gate_w, L.bias, K)
+        oracle.group(idx, w, E)
+        _, x = oracle.moe(x, *mats, idx, w, residual=x, want_x_next=True)
+        t_layers += time.time() - t1
+        n += 1
+        if time.time() - t0 >= 0.75 * seconds:
+            break
+    codes, meta = synth.make_head(cfg)
+    hq = oracle.qmat(codes[0], meta[0], cfg.vocab, H, 8)
+    v1, t_head = 1024, 0.0
+    while True:
+        t1 = time.time()
+        oracle.head(x, hq, 0, v1)
+        t_head = time.time() - t1
+        if time.time() - t0 >= seconds or v1 >= cfg.vocab:
+            break
+        v1 = min(cfg.vocab, v1 * 2)
+    window_s = cfg.layers * t_layers / n + t_head * cfg.vocab / v1
+    used = oracle.threads()
+    oracle.set_threads(all_threads)
+    return {"value": round(cfg.rows / window_s, 4), "unit": "rows/s", "cores": used, "kind": "oracle",
+            "sample": f"window 0 through layers 0..{n - 1} of the stack ({t_layers / n:.2f} s per layer) and the head "
+                      f"on vocabulary entries 0..{v1 - 1} ({t_head:.2f} s); one window = {cfg.layers} layers + the "
+                      f"whole head, scaled: {window_s:.1f} s; OpenMP threads = {used}"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -602,6 +649,9 @@ def bench_stack(args, torch, synth, sw, DevLayer, to_dev_x):
                          "traffic": None, "kernel": "k_head + k_head_argmax (8-bit head GEMV, vocab 151936)",
                          "avg_launch_us": round(head_us, 3), "algorithmic_bytes_per_launch": round(b_h)},
             "cpu_baseline": None}
+    if args.cpu_seconds > 0:
+        log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget)")
+        line["cpu_baseline"] = cpu_baseline_stack(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
