@@ -65,6 +65,10 @@ def lib():
         L.oracle_accept.argtypes = [I, I, P, P, P, P]; L.oracle_accept.restype = I
         L.oracle_tier_count.argtypes = [I, P, P, ctypes.c_float]; L.oracle_tier_count.restype = None
         L.oracle_tier_select.argtypes = [I, P, P, I, ctypes.c_float, P]; L.oracle_tier_select.restype = I
+        L.oracle_philox4x32_10.argtypes = [P, P, P]; L.oracle_philox4x32_10.restype = None
+        L.oracle_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64]; L.oracle_uniform.restype = D
+        L.oracle_sample.argtypes = [P, I, D, I, D, D, ctypes.c_uint64, ctypes.c_uint64, P]
+        L.oracle_sample.restype = I
         L.oracle_threads.argtypes = []; L.oracle_threads.restype = I
         L.oracle_set_threads.argtypes = [I]; L.oracle_set_threads.restype = None
         _lib = L
@@ -219,6 +223,29 @@ def tier_select(counts, resident, max_swaps, min_gain=1.5):
     sw = np.empty(2 * max(max_swaps, 1), np.int32)
     n = lib().oracle_tier_select(c.size, _p(c), _p(res), int(max_swaps), float(min_gain), _p(sw))
     return res, sw[:2 * n].reshape(n, 2)
+
+
+def philox4x32_10(ctr, key):
+    """The four output words of Philox4x32-10 for counter ctr (4 words) and key (2 words)."""
+    c = _c(ctr, np.uint32); k = _c(key, np.uint32)
+    o = np.empty(4, np.uint32)
+    lib().oracle_philox4x32_10(_p(c), _p(k), _p(o))
+    return o
+
+
+def uniform(seed, position):
+    """The draw's uniform in [0, 1) for (seed, position)."""
+    return lib().oracle_uniform(int(seed) & (2**64 - 1), int(position) & (2**64 - 1))
+
+
+def sample(logits, temperature, top_k, top_p=1.0, min_p=0.0, seed=0, position=0):
+    """A sampled token from one row's logits [V] (see oracle_sample). Returns (token,
+    margin: the smallest relative distance of a decision to its boundary)."""
+    lg = _c(logits, np.float32)
+    m = ctypes.c_double(0.0)
+    t = lib().oracle_sample(_p(lg), lg.size, float(temperature), int(top_k), float(top_p), float(min_p),
+                            int(seed) & (2**64 - 1), int(position) & (2**64 - 1), ctypes.byref(m))
+    return t, m.value
 
 
 def threads():

@@ -347,6 +347,135 @@ int oracle_accept(int n_slots, int mtp, const int32_t* argmax, const int32_t* pr
   return kept;
 }
 
+/* ------------------------------------------------------------------ sampled draw */
+
+/*
+ * Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel
+ * random numbers: as easy as 1, 2, 3", SC'11), written from the paper's definition: ten
+ * rounds over a 128-bit counter (c0, c1, c2, c3) with a 64-bit key (k0, k1). A round takes
+ * the two 64-bit products M0 * c0 and M1 * c2 (M0 = 0xD2511F53, M1 = 0xCD9E8D57) and
+ * forms (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); between rounds
+ * the key advances by the Weyl constants (0x9E3779B9, 0xBB67AE85).
+ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; round++) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/*
+ * The draw of one row (Strata docs/BATCHING.md, "Exactness": sampled rows are drawn one
+ * by one with the single-request window's counter-based draw, Philox(seed, position)).
+ * Reading: the key is the request's 64-bit seed (low word first), the counter the row's
+ * 64-bit position (low word first) and two zero words; the uniform is the first two output
+ * words as a 53-bit fraction, u = (out0 * 2^21 + out1 / 2^11) / 2^53 in [0, 1).
+ */
+double oracle_uniform(uint64_t seed, uint64_t position) {
+  const uint32_t ctr[4] = {(uint32_t)position, (uint32_t)(position >> 32), 0u, 0u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t o[4];
+  oracle_philox4x32_10(ctr, key, o);
+  const uint64_t m = ((uint64_t)o[0] << 21) | (uint64_t)(o[1] >> 11);
+  return ldexp((double)m, -53);
+}
+
+/*
+ * A sampled token from one row's logits [V] (the head's output), with the request's
+ * temperature, top_k, top_p, min_p and seed, at the row's position. Readings where the
+ * pages name the parameters only:
+ *   1. candidates: the top_k largest logits (ties to the lower index), top_k clamped to
+ *      1 .. min(128, V), listed by logit descending, then index ascending;
+ *   2. temperature <= 0: the first candidate (greedy: the lowest index of the largest
+ *      logit); else p_j = exp((l_j - l_0) / T) (l_0 the largest), unnormalised;
+ *   3. top_p: the shortest prefix of the list whose sum reaches top_p times the sum of
+ *      all candidates (top_p >= 1: the whole list);
+ *   4. min_p: the prefix of candidates with p_j >= min_p (min_p times the largest, which
+ *      is 1); the kept prefix is the shorter of the two, at least one candidate;
+ *   5. with S the sum of the kept p_j and u = oracle_uniform(seed, position), the token is
+ *      the first kept candidate whose running sum exceeds u * S.
+ * All in double, j ascending. *margin (may be NULL) receives the smallest relative
+ * distance of a decision to its boundary (the running sum against u * S, the top_p and
+ * min_p cuts), so a test can tell the decisions another summation order might flip.
+ */
+int oracle_sample(const float* logits, int V, double temperature, int top_k, double top_p, double min_p,
+                  uint64_t seed, uint64_t position, double* margin) {
+  int K = top_k < 1 ? 1 : top_k;
+  if (K > 128) K = 128;
+  if (K > V) K = V;
+  int cand[128];
+  char* taken = (char*)calloc((size_t)V, 1);
+  for (int j = 0; j < K; j++) {
+    int best = -1;
+    for (int v = 0; v < V; v++) {
+      if (taken[v]) continue;
+      if (best < 0 || logits[v] > logits[best]) best = v; /* strict '>' keeps the lower index */
+    }
+    taken[best] = 1;
+    cand[j] = best;
+  }
+  free(taken);
+  double mg = INFINITY;
+  if (!(temperature > 0.0)) {
+    if (margin) *margin = mg;
+    return cand[0];
+  }
+  double p[128], all = 0.0;
+  for (int j = 0; j < K; j++) {
+    p[j] = exp(((double)logits[cand[j]] - (double)logits[cand[0]]) / temperature);
+    all += p[j];
+  }
+  int mp = K;
+  if (top_p < 1.0) {
+    double c = 0.0;
+    for (int j = 0; j < K; j++) {
+      c += p[j];
+      if (c >= top_p * all) {
+        mp = j + 1;
+        mg = fmin(mg, fabs(c - top_p * all) / all);
+        if (j > 0) mg = fmin(mg, fabs(c - p[j] - top_p * all) / all);
+        break;
+      }
+    }
+  }
+  int mm = 1;
+  while (mm < K && p[mm] >= min_p) mm++;
+  if (min_p > 0.0) {
+    mg = fmin(mg, fabs(p[mm - 1] - min_p));
+    if (mm < K) mg = fmin(mg, fabs(p[mm] - min_p));
+  }
+  const int m = mp < mm ? mp : mm;
+  double S = 0.0;
+  for (int j = 0; j < m; j++) S += p[j];
+  const double t = oracle_uniform(seed, position) * S;
+  double c = 0.0;
+  int pick = m - 1;
+  for (int j = 0; j < m; j++) {
+    c += p[j];
+    if (c > t) {
+      pick = j;
+      break;
+    }
+  }
+  /* the running sums on either side of the pick */
+  c = 0.0;
+  for (int j = 0; j < m; j++) {
+    c += p[j];
+    if (j == pick - 1 || j == pick) mg = fmin(mg, fabs(c - t) / S);
+  }
+  if (margin) *margin = mg;
+  return cand[pick];
+}
+
 /* ---------------------------------------------------------- routing counts and tier */
 
 /*
