@@ -266,6 +266,49 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
                          int32_t* n_accepted, void* const* prof_events);
 
 /*
+ * strata_sample_params - one row's sampling parameters (device memory, one per row).
+ *   temperature <= 0: greedy (the lowest index of the largest logit); else the logits are
+ *               divided by it before the softmax
+ *   top_k       candidates: the top_k largest logits (ties to the lower index); clamped to
+ *               1 .. min(STRATA_MAX_SAMPLE_TOPK, vocab)
+ *   top_p       the shortest prefix of the candidates (by probability, descending) whose
+ *               mass reaches top_p of theirs is kept (>= 1: all)
+ *   min_p       candidates below min_p times the largest probability are dropped
+ *   seed        the request's seed: the key of the draw
+ */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  float min_p;
+  uint64_t seed;
+} strata_sample_params;
+enum { STRATA_MAX_SAMPLE_TOPK = 128 };
+
+/*
+ * strata_window_sample - the sampled token of every row of the window (Strata
+ * docs/BATCHING.md, "Exactness": sampled requests are drawn row by row with the
+ * single-request window's counter-based draw, Philox(seed, position)).
+ *   logits   [rows][vocab] float (strata_window_head's logits)
+ *   params   [rows] strata_sample_params (device); position [rows] int64 (device): the
+ *            token position each row is drawn at (with MTP, a slot's proposal row is at its
+ *            token row's position + 1)
+ *   tokens   [rows] int32 out
+ * The draw: u in [0, 1) from Philox4x32-10 (Salmon et al., SC'11) with counter (position
+ * low word, high word, 0, 0) and key (seed low word, high word), the first two output words
+ * as a 53-bit fraction; p_j = exp((l_j - l_0) / temperature) over the candidates (l_0 the
+ * largest), in double; the kept candidates are the shorter of the top_p and min_p
+ * prefixes (at least one); the token is the first kept candidate whose running sum of p_j
+ * exceeds u times their sum. A slot's MTP proposal is verified by strata_window_accept
+ * with these tokens in place of the argmax (kept when equal to its token row's draw).
+ * Errors: STRATA_EINVAL for rows outside 1..8, vocab < 1, or a NULL / misaligned pointer.
+ * One workgroup per row; no workspace.
+ */
+int strata_window_sample(void* stream, const float* logits, int rows, int vocab,
+                         const strata_sample_params* params, const int64_t* position,
+                         int32_t* tokens, void* const* prof_events);
+
+/*
  * strata_window_tier - routing counts of the window and the adaptive tier's swap choice
  * (Strata docs/BATCHING.md, the paragraph on batch windows counting the experts they
  * route to, with --adapt-every, --adapt-decay and --adapt-min-gain: the windows' routing

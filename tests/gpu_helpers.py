@@ -114,9 +114,12 @@ def row_rel_err(g, o):
 
 
 # The element-wise error: |gpu - oracle| over max(|oracle|, 1e-3 * the row's max |oracle|),
-# reported beside the row metric and held to ELEM_TOL.
+# reported beside the row metric. Near zero it is 1000 times the error relative to the
+# row's max: float32 accumulation of a row (every product exact, sums of up to 4096 terms)
+# has measured 1.7e-5 of the row's max at worst (1.3e-2 in this metric), so 5e-2 bounds the
+# error of the smallest elements 40 times tighter than the row tolerance does.
 ELEM_FLOOR = 1e-3
-ELEM_TOL = None
+ELEM_TOL = 5e-2
 
 
 def elem_rel_err(g, o):

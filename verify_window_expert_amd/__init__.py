@@ -70,6 +70,8 @@ def library():
         L.strata_window_layer_noalloc.restype = I
         L.strata_window_accept.argtypes = [P, P, I, I, I, P, P, P, P, P]
         L.strata_window_accept.restype = I
+        L.strata_window_sample.argtypes = [P, P, I, I, P, P, P, P]
+        L.strata_window_sample.restype = I
         L.strata_window_tier.argtypes = [P, P, I, P, ctypes.c_float, P, I, ctypes.c_float, P, P, P]
         L.strata_window_tier.restype = I
         L.strata_window_stack.argtypes = [P, P, I, I, I, I, I, I, I, I, ctypes.POINTER(CLayer),
@@ -443,6 +445,36 @@ def strata_window_accept(argmax, proposal=None, mtp=True, tokens=None, n_tokens=
                                           _ptr(proposal) if mtp else None, _ptr(tokens), _ptr(n_tokens),
                                           _ptr(n_accepted), _events(prof)))
     return tokens, n_tokens, n_accepted
+
+
+SAMPLE_PARAMS_BYTES = 24
+
+
+def sample_params(rows, device="cuda"):
+    """Device array of per-row sampling parameters (strata_sample_params) from a list of
+    (temperature, top_k, top_p, min_p, seed) tuples, one per row."""
+    import numpy as np
+    dt = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p", "<f4"), ("min_p", "<f4"),
+                   ("seed", "<u8")])
+    assert dt.itemsize == SAMPLE_PARAMS_BYTES
+    a = np.array([tuple(r) for r in rows], dtype=dt)
+    return torch.from_numpy(a.view(np.uint8).copy()).to(device)
+
+
+def strata_window_sample(logits, params, position, tokens=None, stream=None, prof=None):
+    """Sampled token per row (see strata_window_sample). logits: float32 [rows, vocab];
+    params: sample_params(...) of the rows; position: int64 [rows]. Returns int32 [rows]."""
+    _need(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be float32 [rows, vocab]")
+    rows, vocab = logits.shape
+    _need_buf(params, "params", torch.uint8, rows * SAMPLE_PARAMS_BYTES)
+    _need_buf(position, "position", torch.int64, rows)
+    tokens = torch.empty(max(rows, 4), dtype=torch.int32, device=logits.device) if tokens is None else tokens
+    _need_buf(tokens, "tokens", torch.int32, rows)
+    _check(library().strata_window_sample(_stream(stream), _ptr(logits), rows, vocab, _ptr(params), _ptr(position),
+                                          _ptr(tokens), _events(prof)))
+    return tokens[:rows]
 
 
 def strata_window_stream_read(src, sink, magic=0x9E3779B9, stream=None, prof=None):

@@ -547,6 +547,23 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
   return launch_status(sw::launch_accept(a, (hipStream_t)stream, prof_events ? &pa : nullptr), "accept");
 }
 
+int strata_window_sample(void* stream, const float* logits, int rows, int vocab, const strata_sample_params* params,
+                         const int64_t* position, int32_t* tokens, void* const* prof_events) {
+  g_err[0] = 0;
+  if (rows < 1 || rows > STRATA_MAX_ROWS) return fail(STRATA_EINVAL, "rows %d outside 1..%d", rows, STRATA_MAX_ROWS);
+  if (vocab < 1) return fail(STRATA_EINVAL, "vocab %d < 1", vocab);
+  const void* p[] = {logits, params, position, tokens};
+  const char* nm[] = {"logits", "params", "position", "tokens"};
+  for (int i = 0; i < 4; i++)
+    if (!p[i] || !aligned(p[i], 16)) return fail(STRATA_EINVAL, "%s NULL or not 16-byte aligned", nm[i]);
+  static_assert(sizeof(strata_sample_params) == sizeof(sw::SampleParams), "parameter layouts");
+  sw::SampleArgs a;
+  a.logits = logits; a.rows = rows; a.vocab = vocab;
+  a.params = (const sw::SampleParams*)params; a.position = position; a.tokens = tokens;
+  const sw::Prof ps = prof(prof_events, 0);
+  return launch_status(sw::launch_sample(a, (hipStream_t)stream, prof_events ? &ps : nullptr), "sample");
+}
+
 int strata_window_stream_read(void* stream, const void* src, size_t bytes, uint32_t* sink, uint32_t magic,
                               void* const* prof_events) {
   g_err[0] = 0;

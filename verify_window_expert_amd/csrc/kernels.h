@@ -63,6 +63,18 @@ struct AcceptArgs {
   int32_t* tokens; int32_t* n_tokens; int32_t* n_accepted;
 };
 
+// One row's sampling parameters (the layout of strata_sample_params).
+struct SampleParams {
+  float temperature; int32_t top_k; float top_p; float min_p; uint64_t seed;
+};
+
+struct SampleArgs {
+  const float* logits; int rows, vocab;
+  const SampleParams* params;   // [rows]
+  const int64_t* position;      // [rows]
+  int32_t* tokens;              // [rows]
+};
+
 struct TierArgs {
   const uint8_t* row_mask; int n_experts;
   float* counts; float decay;
@@ -138,6 +150,7 @@ int launch_combine_route(const CombineRouteArgs& c, int res_f32, hipStream_t s, 
 size_t down_lds_bytes(int ffn);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
+int launch_sample(const SampleArgs& a, hipStream_t s, const Prof* p);
 int launch_tier(const TierArgs& a, hipStream_t s, const Prof* p);
 int launch_stream_read(const StreamArgs& a, hipStream_t s, const Prof* p);
 int head_workgroups(int vocab);
