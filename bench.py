@@ -318,12 +318,19 @@ def events(torch, n):
 
 def window_tail_kernels(torch, sw, st, cfg, P):
     """Average durations (us, events recorded by the dispatches) of the window's small
-    steps after the layer: the greedy verify/accept of the slots' proposals (rows as
-    token/proposal pairs, argmax and proposals synthetic) and the routing counts of the
-    adaptive tier (count-only windows and selection rounds), from the steps' routing."""
+    steps after the layer: the sampled draw of the window's rows from vocabulary-151936
+    logits (N(0, 3^2), temperature 0.8, top_k 64, top_p 0.95, min_p 0.02), the greedy
+    verify/accept of the slots' proposals (rows as token/proposal pairs, argmax and
+    proposals synthetic) and the routing counts of the adaptive tier (count-only windows
+    and selection rounds), from the steps' routing."""
     R, E = cfg.rows, cfg.experts
     g = torch.Generator(device="cpu").manual_seed(7)
-    argmax = torch.randint(0, 151936, (R,), generator=g, dtype=torch.int32).cuda()
+    V = 151936
+    logits = (torch.randn(R, V, generator=g) * 3).cuda()
+    sparams = sw.sample_params([(0.8, 64, 0.95, 0.02, 1000 + r // 2) for r in range(R)])
+    spos = torch.arange(R, dtype=torch.int64).cuda()
+    stok = sw.strata_window_sample(logits, sparams, spos)
+    argmax = torch.randint(0, V, (R,), generator=g, dtype=torch.int32).cuda()
     mtp = R % 2 == 0                        # token/proposal pairs; one row per slot otherwise
     prop = argmax[0::2].clone()
     prop[1::2] += 1                         # half the proposals kept
@@ -331,7 +338,8 @@ def window_tail_kernels(torch, sw, st, cfg, P):
     resident = (torch.arange(E) % 3 == 0).to(torch.uint8).cuda()
     tok, ntok, nacc = sw.strata_window_accept(argmax, prop, mtp=mtp)
     out = {}
-    for name, fn in (("accept", lambda i, ev: sw.strata_window_accept(argmax, prop, mtp=mtp, tokens=tok,
+    for name, fn in (("sample", lambda i, ev: sw.strata_window_sample(logits, sparams, spos, tokens=stok, prof=ev)),
+                     ("accept", lambda i, ev: sw.strata_window_accept(argmax, prop, mtp=mtp, tokens=tok,
                                                                       n_tokens=ntok, n_accepted=nacc, prof=ev)),
                      ("tier_count", lambda i, ev: sw.strata_window_tier(st.routes[i].row_mask, counts, 0.875,
                                                                         prof=ev)),

@@ -310,6 +310,74 @@ __device__ __forceinline__ void mac_kgroup(const KGroup<BITS>& k0, const KGroup<
   }
 }
 
+// The dot-product form of mac_kgroup (bf16 activations only), for comparison with the
+// matrix cores: lane (n = l % 16, j = l / 16) takes, for each of the window's rows r < R,
+// the dot of its 8 codes of a block (as the exact bf16 values 128 + q) with the row's
+// same 8 inputs (v_dot2_f32_bf16, four per block and row) and adds scale x dot; the lane of
+// j = 0 also adds (min - 128 scale) x the block's sum of the row's inputs. Absent rows cost
+// nothing. The 4 lanes of a row n are summed at the item's end (sum_q).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8_bf16(const bf16x8& a, const bf16x8& b) {
+  const u32x4 ua = __builtin_bit_cast(u32x4, a), ub = __builtin_bit_cast(u32x4, b);
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    // each word into a plain variable first: a bit cast of a vector-element expression
+    // reads the vector's first element
+    const uint32_t wa = ua[i], wb = ub[i];
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa), __builtin_bit_cast(bf16x2, wb), d, false);
+  }
+  return d;
+}
+
+template <int BITS>
+__device__ __forceinline__ void mac_kgroup_valu(const KGroup<BITS>& k0, const KGroup<BITS>& k1, const ActLds& l, int R,
+                                                int g, const CodeConsts& cc, float (&ag)[kMaxRows],
+                                                float (&au)[kMaxRows]) {
+  constexpr int NB = KGroup<BITS>::NB;
+  const int q = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int h = 0; h < NB / 4; h++) {
+    uint32_t m0[4], m1[4];
+    gather_rows(k0.meta[h], m0);
+    gather_rows(k1.meta[h], m1);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int beta = 4 * h + b, blk = g * NB + beta;
+      const bf16x8 wg = code_operand<BITS>(k0, beta, cc), wu = code_operand<BITS>(k1, beta, cc);
+      const float sg = f16_lo(m0[b]), su = f16_lo(m1[b]);
+      const float cg = q == 0 ? fmaf(-128.f, sg, f16_hi(m0[b])) : 0.f;
+      const float cu = q == 0 ? fmaf(-128.f, su, f16_hi(m1[b])) : 0.f;
+#pragma unroll
+      for (int r = 0; r < kMaxRows; r++) {
+        if (r < R) {
+          const bf16x8 xv = *(const bf16x8*)(l.xs + (size_t)r * l.stride + blk * 32 + q * 8);
+          const float sx = l.sx[blk * 16 + r];
+          ag[r] = fmaf(cg, sx, fmaf(sg, dot8_bf16(wg, xv), ag[r]));
+          au[r] = fmaf(cu, sx, fmaf(su, dot8_bf16(wu, xv), au[r]));
+        }
+      }
+    }
+  }
+}
+
+// v summed over the 4 lanes l % 16 + 16 j (j = 0..3), in every one of them: the halves of
+// the wave exchange, then neighbouring rows of 16 ((v_j + v_j^2) + (v_j^1 + v_j^3), the
+// same float in all four).
+__device__ __forceinline__ float sum_q(float v) {
+  const int j = (threadIdx.x & 63) >> 4;
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v += __uint_as_float(j < 2 ? p32[1] : p32[0]);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v += __uint_as_float((j & 1) ? p16[0] : p16[1]);
+  return v;
+}
+
+#ifndef SW_GU_VALU
+#define SW_GU_VALU 0
+#endif
+
 // ------------------------------------------------------------------------ gate / up
 // Persistent, one 8-wave workgroup per compute unit. A worker is a group of S waves of
 // one workgroup (S = 2 when the k-groups split evenly and LDS holds the partial sums,
@@ -489,6 +557,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   const ActLane al = act_lane(l, (c & 7) < R && (c < 8 || F32IN));
   const CodeConsts cc = code_consts();
   f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+  constexpr bool VALU = SW_GU_VALU && !F32IN;   // the dot-product form (comparison builds)
+  float ag8[kMaxRows], au8[kMaxRows];
+#pragma unroll
+  for (int r = 0; r < kMaxRows; r++) { ag8[r] = 0.f; au8[r] = 0.f; }
   int cu_j = 0, cu_g = 0;
   // h = silu(gate) * up for the item's rows, from the finished sums (lanes < 32 hold
   // rows 0..7), split into its bf16 hi and lo parts (hi | lo << 16, one word) and stored
@@ -515,6 +587,25 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   };
   // after this wave's last k-group of an item
   auto finish_item = [&]() __attribute__((always_inline)) {
+    if constexpr (VALU) {
+      // the 4 lanes of each weight row summed; lanes of j = 0, 1 then hold rows 4j .. 4j + 3
+      // as the matrix-core form's accumulators do
+#pragma unroll
+      for (int r = 0; r < kMaxRows; r++) {
+        ag8[r] = sum_q(ag8[r]);
+        au8[r] = sum_q(au8[r]);
+      }
+      // (a select by mask bits: a plain select of the two elements becomes a load from a
+      // selected address and sends the arrays to scratch memory)
+      const uint32_t odd = 0u - (uint32_t)(q & 1);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        ag[i] = __uint_as_float((__float_as_uint(ag8[4 + i]) & odd) | (__float_as_uint(ag8[i]) & ~odd));
+        au[i] = __uint_as_float((__float_as_uint(au8[4 + i]) & odd) | (__float_as_uint(au8[i]) & ~odd));
+      }
+#pragma unroll
+      for (int r = 0; r < kMaxRows; r++) { ag8[r] = 0.f; au8[r] = 0.f; }
+    }
     if constexpr (F32IN) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {   // hi column r (lanes 0..31) + lo column 8 + r
@@ -566,7 +657,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   };
   run_ring<DEPTH>(units, [&](auto d_, bool refill) __attribute__((always_inline)) {
     constexpr int d = decltype(d_)::value;
-    mac_kgroup<BITS, true>(kgg[d], kgu[d], al, part * NGs + cu_g, cc, ag, au);
+    if constexpr (VALU)
+      mac_kgroup_valu<BITS>(kgg[d], kgu[d], l, R, part * NGs + cu_g, cc, ag8, au8);
+    else
+      mac_kgroup<BITS, true>(kgg[d], kgu[d], al, part * NGs + cu_g, cc, ag, au);
     if (refill) issue_next(d_, lds_of);
     if (++cu_g == NGs) {
       finish_item();
