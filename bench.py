@@ -329,7 +329,8 @@ def window_tail_kernels(torch, sw, st, cfg, P):
     logits = (torch.randn(R, V, generator=g) * 3).cuda()
     sparams = sw.sample_params([(0.8, 64, 0.95, 0.02, 1000 + r // 2) for r in range(R)])
     spos = torch.arange(R, dtype=torch.int64).cuda()
-    stok = sw.strata_window_sample(logits, sparams, spos)
+    sws = sw.workspace(sw.workspace_bytes(5, R, 0, vocab=V))
+    stok = sw.strata_window_sample(logits, sparams, spos, ws=sws)
     argmax = torch.randint(0, V, (R,), generator=g, dtype=torch.int32).cuda()
     mtp = R % 2 == 0                        # token/proposal pairs; one row per slot otherwise
     prop = argmax[0::2].clone()
@@ -338,7 +339,8 @@ def window_tail_kernels(torch, sw, st, cfg, P):
     resident = (torch.arange(E) % 3 == 0).to(torch.uint8).cuda()
     tok, ntok, nacc = sw.strata_window_accept(argmax, prop, mtp=mtp)
     out = {}
-    for name, fn in (("sample", lambda i, ev: sw.strata_window_sample(logits, sparams, spos, tokens=stok, prof=ev)),
+    for name, fn in (("sample", lambda i, ev: sw.strata_window_sample(logits, sparams, spos, tokens=stok, ws=sws,
+                                                                      prof=ev)),
                      ("accept", lambda i, ev: sw.strata_window_accept(argmax, prop, mtp=mtp, tokens=tok,
                                                                       n_tokens=ntok, n_accepted=nacc, prof=ev)),
                      ("tier_count", lambda i, ev: sw.strata_window_tier(st.routes[i].row_mask, counts, 0.875,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define STRATA_WINDOW_ABI_VERSION 5
+#define STRATA_WINDOW_ABI_VERSION 6
 
 enum { STRATA_OK = 0, STRATA_EINVAL = -1, STRATA_EUNSUPPORTED = -2, STRATA_EHIP = -3 };
 enum { STRATA_F32 = 0, STRATA_BF16 = 1 };       /* activation dtypes                */
@@ -294,6 +294,8 @@ enum { STRATA_MAX_SAMPLE_TOPK = 128 };
  *            token position each row is drawn at (with MTP, a slot's proposal row is at its
  *            token row's position + 1)
  *   tokens   [rows] int32 out
+ *   ws       at least strata_window_workspace(5, rows, ..., vocab) bytes of scratch: each
+ *            4096-logit chunk's best candidates (contents on entry do not matter)
  * The draw: u in [0, 1) from Philox4x32-10 (Salmon et al., SC'11) with counter (position
  * low word, high word, 0, 0) and key (seed low word, high word), the first two output words
  * as a 53-bit fraction; p_j = exp((l_j - l_0) / temperature) over the candidates (l_0 the
@@ -301,12 +303,16 @@ enum { STRATA_MAX_SAMPLE_TOPK = 128 };
  * prefixes (at least one); the token is the first kept candidate whose running sum of p_j
  * exceeds u times their sum. A slot's MTP proposal is verified by strata_window_accept
  * with these tokens in place of the argmax (kept when equal to its token row's draw).
- * Errors: STRATA_EINVAL for rows outside 1..8, vocab < 1, or a NULL / misaligned pointer.
- * One workgroup per row; no workspace.
+ * Logits must not be NaN (infinities are ordered as values).
+ * Errors: STRATA_EINVAL for rows outside 1..8, vocab < 1, a NULL / misaligned pointer, or
+ * a workspace smaller than strata_window_workspace(5, ...).
+ * Two kernels: one workgroup per (4096-logit chunk, row) keeps the chunk's best top_k, one
+ * workgroup per row reduces those to the row's and draws. prof_events: NULL or {start of
+ * the first kernel, end of the second}.
  */
 int strata_window_sample(void* stream, const float* logits, int rows, int vocab,
                          const strata_sample_params* params, const int64_t* position,
-                         int32_t* tokens, void* const* prof_events);
+                         int32_t* tokens, void* ws, size_t ws_bytes, void* const* prof_events);
 
 /*
  * strata_window_tier - routing counts of the window and the adaptive tier's swap choice
@@ -395,7 +401,7 @@ int strata_window_stack(void* stream, const void* x, int x_dtype, int rows, int 
                         void* const* prof_events);
 
 /* Workspace bytes for which = 0 (route), 1 (moe), 2 (head), 3 (layer), 4 (stack; vocab 0
- * without a head); 0 for invalid arguments. */
+ * without a head), 5 (sample: rows and vocab only); 0 for invalid arguments. */
 size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts,
                                int top_k, int vocab);
 

@@ -42,7 +42,7 @@ def test_abi_version(sw):
     """The built library reports the version its header declares."""
     text = open(os.path.join(ROOT, "include", "strata_window.h")).read()
     declared = int(re.search(r"#define STRATA_WINDOW_ABI_VERSION (\d+)", text).group(1))
-    assert declared == 5
+    assert declared == 6
     assert sw.library().strata_window_abi_version() == declared
 
 
@@ -61,6 +61,11 @@ def test_workspace_sizes(sw):
     assert L.strata_window_workspace(0, 0, 2048, 768, 128, 8, 0) == 0      # rows 0
     assert L.strata_window_workspace(0, 9, 2048, 768, 128, 8, 0) == 0      # rows 9
     assert L.strata_window_workspace(7, 8, 2048, 768, 128, 8, 0) == 0      # unknown
+    # the sampled draw: each 4096-logit chunk's 128 candidate keys and indices per row
+    s = L.strata_window_workspace(5, 8, 0, 0, 0, 0, 151936)
+    assert s >= sw.WS_COUNTER_BYTES + 8 * 8 * 38 * 128 and s % 256 == 0
+    assert L.strata_window_workspace(5, 8, 0, 0, 0, 0, 0) == 0             # vocab 0
+    assert L.strata_window_workspace(5, 9, 0, 0, 0, 0, 100) == 0           # rows 9
 
 
 # fake, aligned device addresses: the checks reject the call before anything uses them

@@ -32,9 +32,11 @@ def gpu_sample(logits, params, positions):
 
 
 def oracle_sample(logits, params, positions):
+    """The oracle's draws with the parameters as the kernel reads them (float32)."""
+    f32 = lambda v: float(np.float32(v))
     out, margins = [], []
     for r, (T, k, tp, mp, seed) in enumerate(params):
-        t, m = oracle.sample(logits[r], T, k, tp, mp, seed=seed, position=positions[r])
+        t, m = oracle.sample(logits[r], f32(T), k, f32(tp), f32(mp), seed=seed, position=positions[r])
         out.append(t)
         margins.append(m)
     return np.array(out, np.int32), np.array(margins)
@@ -87,6 +89,28 @@ def test_sample_ties():
     l[3, ::2] = 1.0
     check(l, [(1.0, 40, 1.0, 0.0, 11), (1.0, 45, 1.0, 0.0, 12), (0.5, 100, 0.9, 0.0, 13), (1.0, 17, 1.0, 0.0, 14)],
           [10, 11, 12, 13], "tied logits")
+
+
+def test_sample_special_values_and_sizes():
+    """Signed zeros (equal, so the lower index first), -inf logits, a vocabulary smaller
+    than top_k, one entry, ragged chunk tails, and a vocabulary long enough that each
+    reducing wave takes a second round of chunks (more than 8 x 7 chunks of 4096)."""
+    rng = np.random.default_rng(25)
+    l = -np.abs(rng.standard_normal((4, 9000))).astype(np.float32)
+    l[0, 100], l[0, 200] = -0.0, 0.0          # the largest two, equal
+    l[1, 7], l[1, 8000] = 0.0, -0.0
+    l[2, :] = -np.inf
+    l[2, rng.choice(9000, 50, replace=False)] = rng.standard_normal(50).astype(np.float32)
+    l[3, 4095:4098] = 5.0                      # equal maxima across a chunk boundary
+    g = check(l, [(0.0, 1, 1.0, 0.0, 1), (0.0, 1, 1.0, 0.0, 2), (1.0, 40, 1.0, 0.0, 3), (0.5, 2, 1.0, 0.0, 4)],
+              [1, 2, 3, 4], "signed zeros, -inf, chunk boundary")
+    assert g[0] == 100 and g[1] == 7 and g[3] in (4095, 4096)
+    for V, params in ((5, [(1.0, 40, 1.0, 0.0, 5), (0.7, 128, 0.9, 0.0, 6)]), (1, [(1.0, 40, 0.5, 0.2, 7)]),
+                      (4097, [(1.3, 128, 0.99, 0.0, 8), (0.9, 3, 1.0, 0.0, 9)])):
+        lg = (rng.standard_normal((len(params), V)) * 2).astype(np.float32)
+        check(lg, params, list(range(10, 10 + len(params))), f"vocab {V}")
+    lg = (rng.standard_normal((2, 300000)) * 3).astype(np.float32)
+    check(lg, [(1.0, 128, 0.95, 0.01, 10), (0.6, 64, 1.0, 0.05, 11)], [20, 21], "vocab 300000")
 
 
 def test_sample_window_equals_alone():

@@ -70,7 +70,7 @@ def library():
         L.strata_window_layer_noalloc.restype = I
         L.strata_window_accept.argtypes = [P, P, I, I, I, P, P, P, P, P]
         L.strata_window_accept.restype = I
-        L.strata_window_sample.argtypes = [P, P, I, I, P, P, P, P]
+        L.strata_window_sample.argtypes = [P, P, I, I, P, P, P, P, S, P]
         L.strata_window_sample.restype = I
         L.strata_window_tier.argtypes = [P, P, I, P, ctypes.c_float, P, I, ctypes.c_float, P, P, P]
         L.strata_window_tier.restype = I
@@ -461,7 +461,7 @@ def sample_params(rows, device="cuda"):
     return torch.from_numpy(a.view(np.uint8).copy()).to(device)
 
 
-def strata_window_sample(logits, params, position, tokens=None, stream=None, prof=None):
+def strata_window_sample(logits, params, position, tokens=None, ws=None, stream=None, prof=None):
     """Sampled token per row (see strata_window_sample). logits: float32 [rows, vocab];
     params: sample_params(...) of the rows; position: int64 [rows]. Returns int32 [rows]."""
     _need(logits, "logits")
@@ -472,8 +472,10 @@ def strata_window_sample(logits, params, position, tokens=None, stream=None, pro
     _need_buf(position, "position", torch.int64, rows)
     tokens = torch.empty(max(rows, 4), dtype=torch.int32, device=logits.device) if tokens is None else tokens
     _need_buf(tokens, "tokens", torch.int32, rows)
+    if ws is None:
+        ws = workspace(workspace_bytes(5, rows, 0, vocab=vocab), logits.device)
     _check(library().strata_window_sample(_stream(stream), _ptr(logits), rows, vocab, _ptr(params), _ptr(position),
-                                          _ptr(tokens), _events(prof)))
+                                          _ptr(tokens), _ptr(ws), _ws_bytes(ws), _events(prof)))
     return tokens[:rows]
 
 

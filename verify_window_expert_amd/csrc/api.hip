@@ -68,6 +68,19 @@ HeadWs head_ws(int rows, int vocab) {
   return w;
 }
 
+// the sampled draw: each 4096-logit chunk's best 128 keys, their indices, and a lower bound
+// of its K-th key, per row
+struct SampleWs { size_t key, idx, lo, total; };
+SampleWs sample_ws(int rows, int vocab) {
+  const size_t nc = (size_t)rows * sw::sample_chunks(vocab), n = nc * 128;
+  SampleWs w;
+  w.key = STRATA_WS_COUNTER_BYTES;
+  w.idx = round_up(w.key + 4 * n, 256);
+  w.lo = round_up(w.idx + 4 * n, 256);
+  w.total = round_up(w.lo + 4 * nc, 256);
+  return w;
+}
+
 // the stack: one layer's workspace (reused by every layer), the two bf16 inputs of the
 // layers after the first (ping-pong), and the head's
 struct StackWs { LayerWs layer; size_t xa, xb, head; HeadWs hw; size_t total; };
@@ -208,6 +221,7 @@ int strata_window_abi_version(void) { return STRATA_WINDOW_ABI_VERSION; }
 const char* strata_window_last_error(void) { return g_err; }
 
 size_t strata_window_workspace(int which, int rows, int hidden, int ffn, int n_experts, int top_k, int vocab) {
+  if (which == 5) return (rows >= 1 && rows <= STRATA_MAX_ROWS && vocab >= 1) ? sample_ws(rows, vocab).total : 0;
   if (rows < 1 || rows > STRATA_MAX_ROWS || hidden < 1) return 0;
   switch (which) {
     case 0: return n_experts >= 1 ? route_ws(rows, hidden, n_experts).total : 0;
@@ -548,18 +562,25 @@ int strata_window_accept(void* stream, const int32_t* argmax, int rows, int n_sl
 }
 
 int strata_window_sample(void* stream, const float* logits, int rows, int vocab, const strata_sample_params* params,
-                         const int64_t* position, int32_t* tokens, void* const* prof_events) {
+                         const int64_t* position, int32_t* tokens, void* ws, size_t ws_bytes,
+                         void* const* prof_events) {
   g_err[0] = 0;
   if (rows < 1 || rows > STRATA_MAX_ROWS) return fail(STRATA_EINVAL, "rows %d outside 1..%d", rows, STRATA_MAX_ROWS);
   if (vocab < 1) return fail(STRATA_EINVAL, "vocab %d < 1", vocab);
-  const void* p[] = {logits, params, position, tokens};
-  const char* nm[] = {"logits", "params", "position", "tokens"};
-  for (int i = 0; i < 4; i++)
+  const void* p[] = {logits, params, position, tokens, ws};
+  const char* nm[] = {"logits", "params", "position", "tokens", "ws"};
+  for (int i = 0; i < 5; i++)
     if (!p[i] || !aligned(p[i], 16)) return fail(STRATA_EINVAL, "%s NULL or not 16-byte aligned", nm[i]);
+  const SampleWs w = sample_ws(rows, vocab);
+  if (ws_bytes < w.total) return fail(STRATA_EINVAL, "workspace %zu bytes < %zu", ws_bytes, w.total);
   static_assert(sizeof(strata_sample_params) == sizeof(sw::SampleParams), "parameter layouts");
   sw::SampleArgs a;
   a.logits = logits; a.rows = rows; a.vocab = vocab;
   a.params = (const sw::SampleParams*)params; a.position = position; a.tokens = tokens;
+  a.chunks = sw::sample_chunks(vocab);
+  a.cand_key = (uint32_t*)((char*)ws + w.key);
+  a.cand_idx = (uint32_t*)((char*)ws + w.idx);
+  a.cand_lo = (uint32_t*)((char*)ws + w.lo);
   const sw::Prof ps = prof(prof_events, 0);
   return launch_status(sw::launch_sample(a, (hipStream_t)stream, prof_events ? &ps : nullptr), "sample");
 }

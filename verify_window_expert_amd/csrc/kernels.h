@@ -73,6 +73,10 @@ struct SampleArgs {
   const SampleParams* params;   // [rows]
   const int64_t* position;      // [rows]
   int32_t* tokens;              // [rows]
+  int chunks;                   // sample_chunks(vocab)
+  uint32_t* cand_key;           // [rows][chunks][128]: each chunk's best keys (workspace)
+  uint32_t* cand_idx;           // [rows][chunks][128]: their indices
+  uint32_t* cand_lo;            // [rows][chunks]: a key at most each chunk's K-th largest
 };
 
 struct TierArgs {
@@ -151,6 +155,7 @@ size_t down_lds_bytes(int ffn);
 int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p);
 int launch_accept(const AcceptArgs& a, hipStream_t s, const Prof* p);
 int launch_sample(const SampleArgs& a, hipStream_t s, const Prof* p);
+int sample_chunks(int vocab);   // 4096-logit chunks of a row in the sampled draw
 int launch_tier(const TierArgs& a, hipStream_t s, const Prof* p);
 int launch_stream_read(const StreamArgs& a, hipStream_t s, const Prof* p);
 int head_workgroups(int vocab);
