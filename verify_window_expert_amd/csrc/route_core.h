@@ -151,7 +151,9 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
       l[u] = ok ? sum + (a.bias ? (double)g.bias[u] : 0.0) : -INFINITY;
       hk[u] = ok ? select_key(l[u], ee) : 0ull;   // 0: below every real key (whose upper half is > 0)
     }
-    // the threshold on the upper halves: the largest T with at least K upper halves >= T
+    // the threshold on the upper halves: the largest T with at least K upper halves >= T;
+    // a trial value with exactly K at or above it already separates the selection (the
+    // same set), and ends the search
     uint32_t hi[MU];
 #pragma unroll
     for (int u = 0; u < MU; u++) hi[u] = (uint32_t)(hk[u] >> 32);
@@ -161,7 +163,10 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, const RouteRegs
       int cnt = 0;
 #pragma unroll
       for (int u = 0; u < MU; u++) cnt += __popcll(__ballot(hi[u] >= cand));
-      if (cnt >= K) T = cand;
+      if (cnt >= K) {
+        T = cand;
+        if (cnt == K) break;
+      }
     }
     int above = 0, at = 0;
 #pragma unroll
