@@ -258,26 +258,34 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(HeadArgs a) {
   }
 }
 
-// Per-row argmax over the workgroups' candidates (one workgroup, after k_head).
-__global__ __launch_bounds__(256) void k_head_argmax(HeadArgs a, int nwg) {
-  const int R = a.rows;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int r = wave; r < R; r += 4) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    for (int w = lane; w < nwg; w += kWave) {
-      const float v = a.part_val[(long)w * R + r];
-      const int id = a.part_idx[(long)w * R + r];
-      if (v > bv || (v == bv && id < bi)) { bv = v; bi = id; }
-    }
+// Per-row argmax over the workgroups' candidates (one workgroup, after k_head): wave r
+// takes row r, every lane loading all its candidates at once (past the last workgroup,
+// the last one's again: a repeated candidate does not change an argmax), then a reduction
+// over the lanes; ties go to the lower index throughout.
+constexpr int kArgmaxPerLane = (kHeadGrid + kWave - 1) / kWave;
+__global__ __launch_bounds__(kMaxRows * kWave) void k_head_argmax(HeadArgs a, int nwg) {
+  const int R = a.rows, r = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (r >= R) return;
+  float v[kArgmaxPerLane];
+  int id[kArgmaxPerLane];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == 0) a.argmax[r] = bi;
+  for (int j = 0; j < kArgmaxPerLane; j++) {
+    const long w = min(lane + kWave * j, nwg - 1);
+    v[j] = a.part_val[w * R + r];
+    id[j] = a.part_idx[w * R + r];
   }
+  float bv = v[0];
+  int bi = id[0];
+#pragma unroll
+  for (int j = 1; j < kArgmaxPerLane; j++)
+    if (v[j] > bv || (v[j] == bv && id[j] < bi)) { bv = v[j]; bi = id[j]; }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  if (lane == 0) a.argmax[r] = bi;
 }
 
 // Greedy verification of the window's proposals (Strata docs/BATCHING.md, --batch-mtp
@@ -334,7 +342,7 @@ int launch_head(const HeadArgs& a, hipStream_t s, const Prof* p) {
   const int e = a.x_dtype == 0 ? launch_head_x<true>(a, lds, nwg, s, p ? &p0 : nullptr)
                                : launch_head_x<false>(a, lds, nwg, s, p ? &p0 : nullptr);
   if (e) return e;
-  launch(k_head_argmax, dim3(1), dim3(256), 0, s, p ? &p1 : nullptr, a, nwg);
+  launch(k_head_argmax, dim3(1), dim3(kMaxRows * kWave), 0, s, p ? &p1 : nullptr, a, nwg);
   return (int)hipGetLastError();
 }
 
