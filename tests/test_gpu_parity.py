@@ -111,6 +111,24 @@ def test_ragged_shapes(layer):
 
 
 @pytest.mark.parametrize("layer", [False, True])
+def test_two_bit_float_input(layer):
+    """2-bit weights with float activations (the staged image's bf16 hi and lo columns, each
+    input divided by its code position's power of two), rows of very different magnitudes
+    (2^-20 .. 2^20): against the oracle, and each row of the window equal to that row alone,
+    bit for bit."""
+    cfg = synth.config("small_f32", hidden=1024, ffn=512, experts=16, top_k=4, rows=6, bits=2)
+    x = synth.make_window(cfg, 2)
+    x *= (2.0 ** np.array([-20, -7, 0, 3, 11, 20]))[:, None].astype(np.float32)
+    check_window(cfg, x=x, layer=layer)
+    L, dl, mats = layer_for(cfg)
+    gr, gout, _ = gpu_window(dl, to_dev_x(x), cfg.top_k, layer=layer)
+    for r in range(cfg.rows):
+        g1, o1, _ = gpu_window(dl, to_dev_x(x[r:r + 1]), cfg.top_k, layer=layer)
+        assert np.array_equal(g1["topk_idx"][0], gr["topk_idx"][r])
+        assert np.array_equal(o1[0], gout[r]), (r, np.max(np.abs(o1[0] - gout[r])))
+
+
+@pytest.mark.parametrize("layer", [False, True])
 def test_all_rows_share_experts(layer):
     cfg = synth.config("small_f32", rows=8, top_k=4)
     x = np.repeat(synth.make_window(cfg, 0)[:1], 8, axis=0)

@@ -275,9 +275,10 @@ __device__ __forceinline__ bf16x8 code_operand(const KGroup<BITS>& kg, int beta,
 
 // Accumulate one k-group of one matrix (or two matrices against the same activations)
 // into acc (C layout: column 4*(l/16)+i, row l%16).
+// The (min - 128 scale) Sx terms go to mn0 / mn1 (which may be acc0 / acc1 themselves).
 template <int BITS, bool TWO>
 __device__ __forceinline__ void mac_kgroup(const KGroup<BITS>& k0, const KGroup<BITS>& k1, const ActLane& al, int g,
-                                           const CodeConsts& cc, f32x4& acc0, f32x4& acc1) {
+                                           const CodeConsts& cc, f32x4& acc0, f32x4& acc1, f32x4& mn0, f32x4& mn1) {
   constexpr int NB = KGroup<BITS>::NB;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -305,8 +306,8 @@ __device__ __forceinline__ void mac_kgroup(const KGroup<BITS>& k0, const KGroup<
     }
     // (min - 128 scale) * Sx of blocks 4h..4h+3 by one fp32 MFMA: the lane supplies
     // block 4h + l/16, exactly the word it loaded
-    acc0 = mfma_f32x4(sx, f16_hi(k0.meta[h]) - 128.f * f16_lo(k0.meta[h]), acc0);
-    if (TWO) acc1 = mfma_f32x4(sx, f16_hi(k1.meta[h]) - 128.f * f16_lo(k1.meta[h]), acc1);
+    mn0 = mfma_f32x4(sx, f16_hi(k0.meta[h]) - 128.f * f16_lo(k0.meta[h]), mn0);
+    if (TWO) mn1 = mfma_f32x4(sx, f16_hi(k1.meta[h]) - 128.f * f16_lo(k1.meta[h]), mn1);
   }
 }
 
@@ -556,7 +557,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
   const int c = lane & 15, q = lane >> 4;
   const ActLane al = act_lane(l, (c & 7) < R && (c < 8 || F32IN));
   const CodeConsts cc = code_consts();
-  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f}, mg = ag, mu = ag;
+  // the min terms accumulate apart from the scale FMAs (mg, mu), except where the
+  // registers would not hold them (2-bit float input at the largest activation sets)
+  constexpr bool SEP_MIN = !(BITS == 2 && F32IN && XG >= 16);
   constexpr bool VALU = SW_GU_VALU && !F32IN;   // the dot-product form (comparison builds)
   float ag8[kMaxRows], au8[kMaxRows];
 #pragma unroll
@@ -605,6 +609,16 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < kMaxRows; r++) { ag8[r] = 0.f; au8[r] = 0.f; }
+    } else if constexpr (SEP_MIN) {
+      // the min terms' accumulators (kept apart so that the scale FMAs of the next blocks
+      // do not wait for each k-group's fp32 MFMA)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        ag[i] += mg[i];
+        au[i] += mu[i];
+      }
+      mg = f32x4{0.f, 0.f, 0.f, 0.f};
+      mu = mg;
     }
     if constexpr (F32IN) {
 #pragma unroll
@@ -660,7 +674,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
     if constexpr (VALU)
       mac_kgroup_valu<BITS>(kgg[d], kgu[d], l, R, part * NGs + cu_g, cc, ag8, au8);
     else
-      mac_kgroup<BITS, true>(kgg[d], kgu[d], al, part * NGs + cu_g, cc, ag, au);
+      mac_kgroup<BITS, true>(kgg[d], kgu[d], al, part * NGs + cu_g, cc, ag, au, SEP_MIN ? mg : ag, SEP_MIN ? mu : au);
     if (refill) issue_next(d_, lds_of);
     if (++cu_g == NGs) {
       finish_item();
@@ -810,14 +824,17 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
   const int c = lane & 15, q = lane >> 4;
   const ActLane al = act_lane(l, (c & 7) < ne);
   const CodeConsts cc = code_consts();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, mn = acc;
   int cu_j = 0, cu_g = 0;
   run_ring<DEPTH>(units, [&](auto d_, bool refill) __attribute__((always_inline)) {
     constexpr int d = decltype(d_)::value;
-    mac_kgroup<BITS, false>(kg[d], kg[d], al, cu_g, cc, acc, acc);
+    mac_kgroup<BITS, false>(kg[d], kg[d], al, cu_g, cc, acc, acc, mn, mn);
     if (refill) issue_next(d_);
     if (++cu_g == NG) {
       const int tile = t0 + cu_j * stride;
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[i] += mn[i];   // the min terms, accumulated apart
+      mn = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[i] += __shfl_down(acc[i], 32);
       if (lane < 32) {
