@@ -393,10 +393,20 @@ __device__ __forceinline__ float sum_q(float v) {
 // round; each wave then requests its first ring of weights and only then stages the
 // activation image in LDS, so the staging overlaps the weights' flight.
 
-constexpr int kGuWaves = 8, kGuThreads = 64 * kGuWaves;
-constexpr size_t kPartBytes = (size_t)kGuWaves * 2 * 32 * 8 * 4;   // [wave][parity][lane < 32][8]
+// Waves of a gate/up workgroup: 16 where a wave's registers fit in 128 (4-bit weights,
+// bf16 activations of at most 4 groups of 8 per thread, i.e. rows * hidden <= 32768), so
+// that one workgroup per compute unit deals the items over 2040 two-wave groups; else 8
+// (1020 groups). The routing core runs once per workgroup either way (its rows on waves
+// 0..7).
+inline int gu_waves_of(int bits, int x_dtype, int rows, int hidden) {
+  return (bits == 4 && x_dtype != 0 && rows * (hidden / 8) <= 4 * 1024) ? 16 : 8;
+}
+// k-split partials: [wave][parity][lane < 32][8]
+constexpr size_t part_bytes(int waves) { return (size_t)waves * 2 * 32 * 8 * 4; }
 
-size_t gateup_split_lds_bytes(int hidden, int x_dtype) { return gateup_lds_bytes(hidden, x_dtype) + kPartBytes; }
+size_t gateup_split_lds_bytes(int hidden, int x_dtype, int bits, int rows) {
+  return gateup_lds_bytes(hidden, x_dtype) + part_bytes(gu_waves_of(bits, x_dtype, rows, hidden));
+}
 size_t route_core_lds_bytes() { return sizeof(RouteLds); }
 
 // s_waitcnt lgkmcnt(0) that the compiler does not move memory operations across
@@ -414,10 +424,12 @@ struct RouteLdsIf<false> {};
 // router's partials and takes the window's tables from its own LDS (one more
 // workgroup, the last, writes the routing outputs and owns no items); otherwise the
 // tables come from strata_route_out.
-template <int BITS, bool F32IN, int XG, bool ROUTED>
-__global__ __launch_bounds__(kGuThreads) void k_gateup(GateUpArgs a) {
+template <int BITS, bool F32IN, int XG, bool ROUTED, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
+void k_gateup(GateUpArgs a) {
   constexpr int DEPTH = kGuDepth;
-  static_assert(kGuThreads == kRouteCoreThreads, "the routing core takes one wave per row");
+  constexpr int kGuWaves = WAVES, kGuThreads = 64 * kGuWaves;
+  static_assert(kGuThreads >= kRouteCoreThreads, "the routing core takes one wave per row");
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_act_g[kMaxSlots];
   __shared__ int s_off_g[kMaxSlots + 1];
@@ -941,26 +953,31 @@ static int persistent_grid(int threads, size_t lds, int max_items, int per_cu_ma
   return max_items < resident ? max_items : resident;
 }
 
-template <int BITS, bool F32IN, int XG, bool ROUTED>
+template <int BITS, bool F32IN, int XG, bool ROUTED, int WAVES = 8>
 static int launch_gateup_k(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
-  auto kern = k_gateup<BITS, F32IN, XG, ROUTED>;
-  if (int e = set_lds<k_gateup<BITS, F32IN, XG, ROUTED>>(lds)) return e;
-  // the fused layer: one more workgroup, which writes the routing outputs. When a compute
-  // unit holds only one of these workgroups, the items get one compute unit fewer, so
-  // that the extra one starts with the others instead of after the first to finish.
-  int grid = persistent_grid<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds, items, 1);
-  if (ROUTED && per_cu<k_gateup<BITS, F32IN, XG, ROUTED>>(kGuThreads, lds) < 2 && grid >= compute_units())
-    grid = compute_units() - 1;
+  auto kern = k_gateup<BITS, F32IN, XG, ROUTED, WAVES>;
+  constexpr int threads = 64 * WAVES;
+  if (int e = set_lds<k_gateup<BITS, F32IN, XG, ROUTED, WAVES>>(lds)) return e;
+  // One workgroup per compute unit. The fused layer has one more workgroup, which writes
+  // the routing outputs: when the grid would fill every slot the compute units hold, the
+  // items get one slot fewer, so that the extra one starts with the others instead of
+  // after the first to finish.
+  const int capacity = compute_units() * per_cu<k_gateup<BITS, F32IN, XG, ROUTED, WAVES>>(threads, lds);
+  int grid = persistent_grid<k_gateup<BITS, F32IN, XG, ROUTED, WAVES>>(threads, lds, items, 1);
+  if (ROUTED && grid + 1 > capacity) grid = capacity - 1;
   grid += ROUTED ? 1 : 0;
-  launch(kern, dim3(grid), dim3(kGuThreads), lds, s, p, a);
+  launch(kern, dim3(grid), dim3(threads), lds, s, p, a);
   return 0;
 }
 
 template <int BITS, bool F32IN, bool ROUTED>
 static int launch_gateup_x(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
   // activation groups of 8 per thread, all loaded up front (rows * hidden / 8 <= 16 * 512
-  // for every hidden whose image fits in LDS)
+  // for every hidden whose image fits in LDS); 16 waves where gu_waves_of says so
+  constexpr int kGuThreads = 64 * 8;
   const int groups = a.rows * (a.hidden / 8);
+  if constexpr (BITS == 4 && !F32IN)
+    if (gu_waves_of(BITS, 1, a.rows, a.hidden) == 16) return launch_gateup_k<BITS, F32IN, 4, ROUTED, 16>(a, lds, items, s, p);
   if (groups <= 4 * kGuThreads) return launch_gateup_k<BITS, F32IN, 4, ROUTED>(a, lds, items, s, p);
   if (groups <= 8 * kGuThreads) return launch_gateup_k<BITS, F32IN, 8, ROUTED>(a, lds, items, s, p);
   if (groups <= 16 * kGuThreads) return launch_gateup_k<BITS, F32IN, 16, ROUTED>(a, lds, items, s, p);
@@ -974,9 +991,10 @@ static int launch_gateup_any(const GateUpArgs& a0, int max_slots, hipStream_t s,
   // two waves per item when the k-groups split evenly and the partial-sum buffers fit
   // next to the activation image
   const int NG = a.hidden / (512 / a.bits);
-  const size_t static_lds = 2048 + (ROUTED ? sizeof(RouteLds) : 0);
-  a.split = (NG % 2 == 0 && gateup_split_lds_bytes(a.hidden, a.x_dtype) + static_lds <= 160 * 1024) ? 2 : 1;
-  const size_t lds = a.split == 2 ? gateup_split_lds_bytes(a.hidden, a.x_dtype) : gateup_lds_bytes(a.hidden, a.x_dtype);
+  const size_t static_lds = 2048 + (ROUTED ? sizeof(RouteLds) : 0);   // (s_cnt, s_done: 256 B at 16 waves)
+  a.split = (NG % 2 == 0 && gateup_split_lds_bytes(a.hidden, a.x_dtype, a.bits, a.rows) + static_lds <= 160 * 1024) ? 2 : 1;
+  const size_t lds = a.split == 2 ? gateup_split_lds_bytes(a.hidden, a.x_dtype, a.bits, a.rows)
+                                  : gateup_lds_bytes(a.hidden, a.x_dtype);
   const int items = max_slots * (a.ffn / 16);
   int e;
   if (a.bits == 4)
