@@ -187,6 +187,26 @@ def test_accept_rejects(sw):
     assert call(nacc=0) == sw.STRATA_EINVAL
 
 
+def test_sample_rejects(sw):
+    """strata_window_sample refuses bad shapes, pointers and a short workspace before it
+    enqueues anything (the fake device addresses are never touched)."""
+    L = sw.library()
+    need = L.strata_window_workspace(5, 8, 0, 0, 0, 0, 151936)
+
+    def call(rows=8, vocab=151936, lg=A, prm=A, pos=A, tok=A, ws=A, wsb=need):
+        return L.strata_window_sample(None, lg, rows, vocab, prm, pos, tok, ws, wsb, None)
+    assert call(rows=0) == sw.STRATA_EINVAL
+    assert call(rows=9) == sw.STRATA_EINVAL
+    assert call(vocab=0) == sw.STRATA_EINVAL
+    assert call(lg=None) == sw.STRATA_EINVAL
+    assert call(prm=A + 8) == sw.STRATA_EINVAL
+    assert call(pos=None) == sw.STRATA_EINVAL
+    assert call(tok=A + 4) == sw.STRATA_EINVAL
+    assert call(ws=None) == sw.STRATA_EINVAL
+    assert call(wsb=need - 1) == sw.STRATA_EINVAL
+    assert "workspace" in L.strata_window_last_error().decode()
+
+
 def test_tier_rejects(sw):
     L = sw.library()
     def call(E=128, rm=A, c=A, decay=1.0, res=A, ms=4, gain=1.5, swp=A, ns=A):
