@@ -28,12 +28,12 @@ def layer_for(cfg):
     return _layers[cfg]
 
 
-def check(cfg, window=0, renorm=False, residual=False, x_next=False):
+def check(cfg, window=0, renorm=False, residual=False, x_next=False, layer=True):
     L, dl, mats = layer_for(cfg)
     x = synth.make_window(cfg, window)
     print(f"[layer] {cfg.name} H={cfg.hidden} E={cfg.experts} bits={cfg.bits} R={x.shape[0]} "
-          f"window={window} renorm={renorm} residual={residual}", flush=True)
-    gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next, layer=True)
+          f"window={window} renorm={renorm} residual={residual} layer={layer}", flush=True)
+    gr, gout, gxn = gpu_window(dl, to_dev_x(x), cfg.top_k, renorm, residual, x_next, layer=layer)
     orc, oout, oxn = oracle_window(L, mats, x, cfg, renorm, residual, x_next)
     assert topk_gap(orc["logits"], cfg.top_k) > 1e-9, "near-tie in the routing of this seed"
     assert_route_equal(gr, orc, cfg)
@@ -75,6 +75,21 @@ def test_layer_row_equals_row_alone_bitwise():
     for r in range(x.shape[0]):
         print(f"[layer] row {r} alone", flush=True)
         _, g1, _ = gpu_window(dl, to_dev_x(x[r:r + 1]), cfg.top_k, layer=True)
+        assert np.array_equal(g1[0].view(np.uint32), gout[r].view(np.uint32)), r
+
+
+@pytest.mark.parametrize("hidden,bits,layer", [(5632, 4, True), (5632, 2, True), (6144, 4, True), (6656, 4, False)])
+def test_row_equals_row_alone_where_the_waves_depend_on_rows(hidden, bits, layer):
+    """bf16 rows at hiddens where the gate/up wave count depends on the window's rows: at
+    5632 a lone row runs 16-wave workgroups and an 8-row window 8-wave ones; at 6144 (fused
+    layer call) and 6656 (two-call path) a lone row would want 16 waves, whose partial sums
+    do not fit next to the activation image. The k-split of a row's sums is fixed by the
+    shapes alone, so each row of the window is bit-identical to the row computed alone."""
+    cfg = synth.config("two_slots_mtp", hidden=hidden, ffn=256, experts=16, top_k=4, rows=8, bits=bits)
+    dl, x, _, gout, _, _ = check(cfg, 0, layer=layer)
+    for r in range(x.shape[0]):
+        print(f"[layer] H={hidden} bits={bits} row {r} alone", flush=True)
+        _, g1, _ = gpu_window(dl, to_dev_x(x[r:r + 1]), cfg.top_k, layer=layer)
         assert np.array_equal(g1[0].view(np.uint32), gout[r].view(np.uint32)), r
 
 

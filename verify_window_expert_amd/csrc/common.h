@@ -108,6 +108,18 @@ __device__ __forceinline__ bf16x8 q2_to_bf16x8(uint32_t word, bool high, const C
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// The same conversion with the byte-permute selector in a register (0x0C010C00: the low
+// half, 0x0C030C02: the high half), so that lanes can take different halves.
+__device__ __forceinline__ bf16x8 q2_to_bf16x8_sel(uint32_t word, uint32_t sel, const CodeConsts& k) {
+  const uint32_t v = __builtin_amdgcn_perm(0u, word, sel);
+  u32x4 w;
+  w[0] = (v & k.m2) | k.magic;
+  w[1] = ((v >> 2) & k.m2) | k.magic;
+  w[2] = ((v >> 4) & k.m2) | k.magic;
+  w[3] = ((v >> 6) & k.m2) | k.magic;
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 // 8-bit signed codes, 4 per word (code i in byte i). Flipping the sign bit gives
 // u = q + 128 in [1, 255]; masking bytes into the mantissa of the binary16 constant
 // 1024.0 (0x6400) gives exactly 1024 + u = 1152 + q. Element order for the 8 codes
@@ -135,6 +147,15 @@ __device__ __forceinline__ void gather_rows(uint32_t v, uint32_t (&out)[4]) {
   const auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);  // {r0 x4}, {r1 x4}
   const auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);  // {r2 x4}, {r3 x4}
   out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+}
+
+// Lane l = 16*q + c holds v_q. Returns, in every lane of column c, out[0] = v_0 in lanes
+// 0..31 and v_1 in lanes 32..63, out[1] = v_2 in lanes 0..31 and v_3 in lanes 32..63
+// (neighbouring rows exchange first, then the halves).
+__device__ __forceinline__ void pair_rows(uint32_t v, uint32_t (&out)[2]) {
+  const auto t = __builtin_amdgcn_permlane16_swap(v, v, false, false);           // {r0 r0 r2 r2}, {r1 r1 r3 r3}
+  const auto u = __builtin_amdgcn_permlane32_swap(t[0], t[1], false, false);     // {r0 r0 r1 r1}, {r2 r2 r3 r3}
+  out[0] = u[0]; out[1] = u[1];
 }
 
 // ------------------------------------------------------------ wave reductions

@@ -218,6 +218,33 @@ __device__ __forceinline__ ActLane act_lane(const ActLds& l, bool col_ok) {
   return al;
 }
 
+// Paired form (bf16 activations: at most 8 of the 16 MFMA columns hold rows). Two
+// blocks b = 2p and b' = 2p + 1 of a k-group share one accumulator tile: columns 0..7
+// take rows 0..7 against block b, columns 8..15 the same rows against block b'. In MFMA
+// m (0, 1) of the pair, lanes of k-slice q supply block b + ((q / 2) xor m) (their own
+// stored inputs 8q..8q+7 of that block), and a lane's activation operand is its row's
+// inputs where that block matches its column half, else the zero row. Over the two
+// MFMAs every input of both blocks meets its row once; lanes 0..31 then hold rows 0..7
+// against b, lanes 32..63 against b', so one scale FMA per lane covers both blocks.
+struct ActLanePair {
+  const uint16_t* row[2];   // MFMA m: + blk * 32 (blk = the pair's first block)
+  const float* sx;
+};
+
+__device__ __forceinline__ ActLanePair act_lane_pair(const ActLds& l, int R) {
+  const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+  const int half = c >> 3, r = c & 7;                 // column half: block b or b'
+  const int m_real = (q >> 1) ^ half;                 // the MFMA whose block matches
+  ActLanePair al;
+#pragma unroll
+  for (int m = 0; m < 2; m++) {
+    const bool real = m == m_real && r < R;
+    al.row[m] = l.xs + (size_t)(real ? r : l.zero_row) * l.stride + half * 32 + q * 8;
+  }
+  al.sx = l.sx + q * 16 + c;
+  return al;
+}
+
 // ---------------------------------------------------------------------------- weights
 // One (matrix, 16-row tile) as two buffer resources: its codes and its metadata from
 // k-group 0 on (the tiled layout of the header: k-group g at g * 1024 code bytes and
@@ -311,6 +338,59 @@ __device__ __forceinline__ void mac_kgroup(const KGroup<BITS>& k0, const KGroup<
   }
 }
 
+// The lane's code operand for MFMA m of pair p of 4-block group h: block
+// 4h + 2p + ((q / 2) xor m). sel2[m] holds the 2-bit half selector for that block; at
+// 4 bits the lane picks one of two stored words.
+template <int BITS>
+__device__ __forceinline__ bf16x8 code_operand_pair(const KGroup<BITS>& kg, int h, int p, int m, bool upper,
+                                                    const uint32_t (&sel2)[2], const CodeConsts& cc) {
+  if constexpr (BITS == 4) {
+    const uint32_t w0 = kg.codes[2 * p], w1 = kg.codes[2 * p + 1];
+    return q4_to_bf16x8((upper != (m != 0)) ? w1 : w0, cc);
+  } else {
+    return q2_to_bf16x8_sel(kg.codes[2 * h + p], sel2[m], cc);
+  }
+}
+
+// mac_kgroup in the paired form (bf16 activations; see ActLanePair). acc holds rows
+// 0..7 against the even blocks in lanes 0..31 and against the odd blocks in lanes
+// 32..63; the min terms (mn) fill lanes 0..31 only, as before.
+template <int BITS, bool TWO>
+__device__ __forceinline__ void mac_kgroup_pair(const KGroup<BITS>& k0, const KGroup<BITS>& k1, const ActLanePair& al,
+                                                int g, const CodeConsts& cc, const uint32_t (&sel2)[2], f32x4& acc0,
+                                                f32x4& acc1, f32x4& mn0, f32x4& mn1) {
+  constexpr int NB = KGroup<BITS>::NB;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const bool upper = (threadIdx.x & 63) >= 32;
+#pragma unroll
+  for (int h = 0; h < NB / 4; h++) {
+    uint32_t m0[2], m1[2];
+    pair_rows(k0.meta[h], m0);
+    if (TWO) pair_rows(k1.meta[h], m1);
+    const float sx = al.sx[(g * NB + 4 * h) * 16];
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const int blk = g * NB + 4 * h + 2 * p;
+      const bf16x8 a0 = *(const bf16x8*)(al.row[0] + blk * 32);
+      const bf16x8 a1 = *(const bf16x8*)(al.row[1] + blk * 32);
+      f32x4 d0 = mfma_bf16(a0, code_operand_pair<BITS>(k0, h, p, 0, upper, sel2, cc), z);
+      d0 = mfma_bf16(a1, code_operand_pair<BITS>(k0, h, p, 1, upper, sel2, cc), d0);
+      const float s0 = f16_lo(m0[p]);
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc0[i] = fmaf(s0, d0[i], acc0[i]);
+      if (TWO) {
+        f32x4 d1 = mfma_bf16(a0, code_operand_pair<BITS>(k1, h, p, 0, upper, sel2, cc), z);
+        d1 = mfma_bf16(a1, code_operand_pair<BITS>(k1, h, p, 1, upper, sel2, cc), d1);
+        const float s1 = f16_lo(m1[p]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc1[i] = fmaf(s1, d1[i], acc1[i]);
+      }
+    }
+    mn0 = mfma_f32x4(sx, f16_hi(k0.meta[h]) - 128.f * f16_lo(k0.meta[h]), mn0);
+    if (TWO) mn1 = mfma_f32x4(sx, f16_hi(k1.meta[h]) - 128.f * f16_lo(k1.meta[h]), mn1);
+  }
+}
+
 // The dot-product form of mac_kgroup (bf16 activations only), for comparison with the
 // matrix cores: lane (n = l % 16, j = l / 16) takes, for each of the window's rows r < R,
 // the dot of its 8 codes of a block (as the exact bf16 values 128 + q) with the row's
@@ -378,6 +458,9 @@ __device__ __forceinline__ float sum_q(float v) {
 #ifndef SW_GU_VALU
 #define SW_GU_VALU 0
 #endif
+#ifndef SW_GU_PAIR
+#define SW_GU_PAIR 1
+#endif
 
 // ------------------------------------------------------------------------ gate / up
 // Persistent, one 8-wave workgroup per compute unit. A worker is a group of S waves of
@@ -393,19 +476,32 @@ __device__ __forceinline__ float sum_q(float v) {
 // round; each wave then requests its first ring of weights and only then stages the
 // activation image in LDS, so the staging overlaps the weights' flight.
 
-// Waves of a gate/up workgroup: 16 where a wave's registers fit in 128 (4-bit weights,
-// bf16 activations of at most 4 groups of 8 per thread, i.e. rows * hidden <= 32768), so
-// that one workgroup per compute unit deals the items over 2040 two-wave groups; else 8
-// (1020 groups). The routing core runs once per workgroup either way (its rows on waves
-// 0..7).
-inline int gu_waves_of(int bits, int x_dtype, int rows, int hidden) {
-  return (bits == 4 && x_dtype != 0 && rows * (hidden / 8) <= 4 * 1024) ? 16 : 8;
+// Waves of a gate/up workgroup: 16 where a wave's registers fit in 128 (bf16 activations
+// of at most 4 groups of 8 per thread, i.e. rows * hidden <= 32768; 4-bit weights, or
+// 2-bit in the fused layer's kernel), so that one workgroup per compute unit deals the
+// items over 2040 two-wave groups; else 8 (1020 groups). The routing core runs once per
+// workgroup either way (its rows on waves 0..7). This choice depends on the window's
+// rows, so it never decides the k-split: see gateup_plan.
+inline bool gu_wants_16(int bits, int x_dtype, int rows, int hidden, bool routed) {
+  return (bits == 4 || (bits == 2 && routed)) && x_dtype != 0 && rows * (hidden / 8) <= 4 * 1024;
 }
 // k-split partials: [wave][parity][lane < 32][8]
 constexpr size_t part_bytes(int waves) { return (size_t)waves * 2 * 32 * 8 * 4; }
 
-size_t gateup_split_lds_bytes(int hidden, int x_dtype, int bits, int rows) {
-  return gateup_lds_bytes(hidden, x_dtype) + part_bytes(gu_waves_of(bits, x_dtype, rows, hidden));
+// The k-split S (1 or 2) from the shapes alone: 2 when the k-groups split evenly and an
+// 8-wave workgroup's partial buffers fit next to the activation image, so that a row's
+// sums are the same in every window. Then the waves: 16 where gu_wants_16 says so and
+// the buffers of 16 waves fit as well (with S = 1 there are none), else 8. Returns the
+// dynamic LDS bytes.
+static size_t gateup_plan(int hidden, int x_dtype, int bits, int rows, bool routed, size_t static_lds, int& split,
+                   int& waves) {
+  constexpr size_t kLds = 160 * 1024;
+  const size_t image = gateup_lds_bytes(hidden, x_dtype);
+  const int NG = hidden / (512 / bits);
+  split = (NG % 2 == 0 && image + part_bytes(8) + static_lds <= kLds) ? 2 : 1;
+  const size_t parts16 = split == 2 ? part_bytes(16) : 0;
+  waves = gu_wants_16(bits, x_dtype, rows, hidden, routed) && image + parts16 + static_lds <= kLds ? 16 : 8;
+  return image + (split == 2 ? part_bytes(waves) : 0);
 }
 size_t route_core_lds_bytes() { return sizeof(RouteLds); }
 
@@ -569,11 +665,16 @@ void k_gateup(GateUpArgs a) {
   const int c = lane & 15, q = lane >> 4;
   const ActLane al = act_lane(l, (c & 7) < R && (c < 8 || F32IN));
   const CodeConsts cc = code_consts();
+  constexpr bool VALU = SW_GU_VALU && !F32IN;   // the dot-product form (comparison builds)
+  constexpr bool PAIR = SW_GU_PAIR && !F32IN && !VALU;   // two blocks per accumulator tile
+  const ActLanePair alp = act_lane_pair(l, R);
+  uint32_t sel2[2];   // 2-bit half selectors of MFMA 0 and 1 (lanes 32..63 start on the odd block)
+  sel2[0] = lane >= 32 ? 0x0C030C02u : 0x0C010C00u;
+  sel2[1] = lane >= 32 ? 0x0C010C00u : 0x0C030C02u;
   f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f}, mg = ag, mu = ag;
   // the min terms accumulate apart from the scale FMAs (mg, mu), except where the
   // registers would not hold them (2-bit float input at the largest activation sets)
   constexpr bool SEP_MIN = !(BITS == 2 && F32IN && XG >= 16);
-  constexpr bool VALU = SW_GU_VALU && !F32IN;   // the dot-product form (comparison builds)
   float ag8[kMaxRows], au8[kMaxRows];
 #pragma unroll
   for (int r = 0; r < kMaxRows; r++) { ag8[r] = 0.f; au8[r] = 0.f; }
@@ -632,13 +733,15 @@ void k_gateup(GateUpArgs a) {
       mg = f32x4{0.f, 0.f, 0.f, 0.f};
       mu = mg;
     }
-    if constexpr (F32IN) {
+    if constexpr (F32IN || PAIR) {
+      // float x: hi column r (lanes 0..31) + lo column 8 + r; paired form: row r against
+      // the even blocks + the odd blocks
 #pragma unroll
-      for (int i = 0; i < 4; i++) {   // hi column r (lanes 0..31) + lo column 8 + r
+      for (int i = 0; i < 4; i++) {
         ag[i] += __shfl_down(ag[i], 32);
         au[i] += __shfl_down(au[i], 32);
       }
-    }   // (bf16 x: the lo columns read the zero row and hold exact zeros)
+    }   // (bf16 x otherwise: the lo columns read the zero row and hold exact zeros)
     if (S == 1) {
       if (lane < 32) write_h(ag, au);
     } else {
@@ -685,6 +788,9 @@ void k_gateup(GateUpArgs a) {
     constexpr int d = decltype(d_)::value;
     if constexpr (VALU)
       mac_kgroup_valu<BITS>(kgg[d], kgu[d], l, R, part * NGs + cu_g, cc, ag8, au8);
+    else if constexpr (PAIR)
+      mac_kgroup_pair<BITS, true>(kgg[d], kgu[d], alp, part * NGs + cu_g, cc, sel2, ag, au, SEP_MIN ? mg : ag,
+                                  SEP_MIN ? mu : au);
     else
       mac_kgroup<BITS, true>(kgg[d], kgu[d], al, part * NGs + cu_g, cc, ag, au, SEP_MIN ? mg : ag, SEP_MIN ? mu : au);
     if (refill) issue_next(d_, lds_of);
@@ -971,13 +1077,13 @@ static int launch_gateup_k(const GateUpArgs& a, size_t lds, int items, hipStream
 }
 
 template <int BITS, bool F32IN, bool ROUTED>
-static int launch_gateup_x(const GateUpArgs& a, size_t lds, int items, hipStream_t s, const Prof* p) {
+static int launch_gateup_x(const GateUpArgs& a, size_t lds, int waves, int items, hipStream_t s, const Prof* p) {
   // activation groups of 8 per thread, all loaded up front (rows * hidden / 8 <= 16 * 512
-  // for every hidden whose image fits in LDS); 16 waves where gu_waves_of says so
+  // for every hidden whose image fits in LDS); 16 waves where gateup_plan says so
   constexpr int kGuThreads = 64 * 8;
   const int groups = a.rows * (a.hidden / 8);
-  if constexpr (BITS == 4 && !F32IN)
-    if (gu_waves_of(BITS, 1, a.rows, a.hidden) == 16) return launch_gateup_k<BITS, F32IN, 4, ROUTED, 16>(a, lds, items, s, p);
+  if constexpr ((BITS == 4 || ROUTED) && !F32IN)
+    if (waves == 16) return launch_gateup_k<BITS, F32IN, 4, ROUTED, 16>(a, lds, items, s, p);
   if (groups <= 4 * kGuThreads) return launch_gateup_k<BITS, F32IN, 4, ROUTED>(a, lds, items, s, p);
   if (groups <= 8 * kGuThreads) return launch_gateup_k<BITS, F32IN, 8, ROUTED>(a, lds, items, s, p);
   if (groups <= 16 * kGuThreads) return launch_gateup_k<BITS, F32IN, 16, ROUTED>(a, lds, items, s, p);
@@ -988,19 +1094,17 @@ template <bool ROUTED>
 static int launch_gateup_any(const GateUpArgs& a0, int max_slots, hipStream_t s, const Prof* p) {
   GateUpArgs a = a0;
   const bool f32 = a.x_dtype == 0;
-  // two waves per item when the k-groups split evenly and the partial-sum buffers fit
-  // next to the activation image
-  const int NG = a.hidden / (512 / a.bits);
   const size_t static_lds = 2048 + (ROUTED ? sizeof(RouteLds) : 0);   // (s_cnt, s_done: 256 B at 16 waves)
-  a.split = (NG % 2 == 0 && gateup_split_lds_bytes(a.hidden, a.x_dtype, a.bits, a.rows) + static_lds <= 160 * 1024) ? 2 : 1;
-  const size_t lds = a.split == 2 ? gateup_split_lds_bytes(a.hidden, a.x_dtype, a.bits, a.rows)
-                                  : gateup_lds_bytes(a.hidden, a.x_dtype);
+  int waves = 8;
+  const size_t lds = gateup_plan(a.hidden, a.x_dtype, a.bits, a.rows, ROUTED, static_lds, a.split, waves);
   const int items = max_slots * (a.ffn / 16);
   int e;
   if (a.bits == 4)
-    e = f32 ? launch_gateup_x<4, true, ROUTED>(a, lds, items, s, p) : launch_gateup_x<4, false, ROUTED>(a, lds, items, s, p);
+    e = f32 ? launch_gateup_x<4, true, ROUTED>(a, lds, waves, items, s, p)
+            : launch_gateup_x<4, false, ROUTED>(a, lds, waves, items, s, p);
   else
-    e = f32 ? launch_gateup_x<2, true, ROUTED>(a, lds, items, s, p) : launch_gateup_x<2, false, ROUTED>(a, lds, items, s, p);
+    e = f32 ? launch_gateup_x<2, true, ROUTED>(a, lds, waves, items, s, p)
+            : launch_gateup_x<2, false, ROUTED>(a, lds, waves, items, s, p);
   return e ? e : (int)hipGetLastError();
 }
 
