@@ -26,6 +26,12 @@ from gpu_helpers import (REL_TOL, assert_close, assert_route_equal, oracle_mats,
 STEPS, LAYERS = 64, 8
 
 
+def bits(t):
+    """The tensor's bytes as integers: equal bit patterns compare equal, NaN included (the
+    routing arrays' padding past the written entries holds whatever the memory held)."""
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
 @pytest.fixture(scope="module")
 def replayed():
     cfg = synth.config("four_slots_mtp_zipf")
@@ -74,9 +80,9 @@ def test_graph_equals_eager(replayed):
         st.out[i].fill_(float("nan"))
         st.step(i)
     torch.cuda.synchronize()
-    assert torch.equal(torch.stack(st.out), outs)
+    assert torch.equal(bits(torch.stack(st.out)), bits(outs))
     for n, t in st.big.items():
-        assert torch.equal(t[:STEPS], routes[n]), n
+        assert torch.equal(bits(t[:STEPS]), bits(routes[n])), n
 
 
 def test_graph_replays_bitwise(replayed):
@@ -87,7 +93,7 @@ def test_graph_replays_bitwise(replayed):
             o.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(torch.stack(st.out), outs), rep
+        assert torch.equal(bits(torch.stack(st.out)), bits(outs)), rep
         for n, t in st.big.items():
-            assert torch.equal(t[:STEPS], routes[n]), (rep, n)
+            assert torch.equal(bits(t[:STEPS]), bits(routes[n])), (rep, n)
     print("[graph] 100 replays bitwise equal", flush=True)
