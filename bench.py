@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -115,10 +116,21 @@ def bpw(bits):
     return bits / 8.0 + 4.0 / 32.0
 
 
+def code_text(path):
+    """A C++ source's code: comments removed, each line stripped, blank lines dropped (so a
+    comment edit leaves the kernel's fingerprint, and its counter summary, valid)."""
+    s = open(path, encoding="utf-8").read()
+    s = re.sub(r"/\*.*?\*/", " ", s, flags=re.S)
+    s = re.sub(r"//[^\n]*", "", s)
+    return "\n".join(ln.strip() for ln in s.split("\n") if ln.strip())
+
+
 def source_sha(files):
+    """sha256 (first 16 hex digits) of the files' code text, in order."""
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        h.update(code_text(os.path.join(ROOT, f)).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -463,10 +463,10 @@ __device__ __forceinline__ float sum_q(float v) {
 #endif
 
 // ------------------------------------------------------------------------ gate / up
-// Persistent, one 8-wave workgroup per compute unit. A worker is a group of S waves of
-// one workgroup (S = 2 when the k-groups split evenly and LDS holds the partial sums,
-// else 1: a choice made from the shapes alone, so that a row's arithmetic is the same
-// in every window); it owns whole items (slot, 16-row ffn tile), and wave p of the group streams k-groups
+// Persistent, one workgroup of 8 or 16 waves per compute unit. A worker is a group of S
+// waves of one workgroup (S = 2 when the k-groups split evenly and LDS holds the
+// partial sums, else 1: a choice made from the shapes alone, so that a row's arithmetic
+// is the same in every window); it owns whole items (slot, 16-row ffn tile), and wave p of the group streams k-groups
 // [p NG/S, (p+1) NG/S) of the item's gate and up rows through the ring. With S = 2 the
 // two partial sums meet in LDS and the second wave to arrive adds them in part order
 // (so the result does not depend on which arrives first) and writes h. Items go to
