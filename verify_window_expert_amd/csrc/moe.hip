@@ -594,7 +594,10 @@ void k_gateup(GateUpArgs a) {
   }
   const int S = a.split;
   const int gw = kGuWaves / S;                     // groups per workgroup
-  const int part = wave / gw, gl = wave % gw;      // part of the k-range; group in the workgroup
+  // part of the k-range and group in the workgroup: a group's waves are adjacent
+  // (wave S gl + p), so that the hardware's round-robin placement puts them on different
+  // SIMDs and a workgroup's first items spread over all four
+  const int part = wave % S, gl = wave / S;
   const int Wg = grid * gw;                        // groups
   const int me = gl * grid + blockIdx.x;           // this wave's group
   const int NGs = NG / S;                          // k-groups per part
@@ -765,8 +768,8 @@ void k_gateup(GateUpArgs a) {
       asm volatile("" ::: "memory");   // no LDS read is hoisted above the arrival
       if (old % 2 == 1) {   // second to arrive: part 0 + part 1, in that order
         if (lane < 32) {
-          const float* p0 = s_part + ((size_t)(gl * 2 + par) * 32 + lane) * 8;          // wave gl: part 0
-          const float* p1 = s_part + ((size_t)((gw + gl) * 2 + par) * 32 + lane) * 8;   // wave gw + gl: part 1
+          const float* p0 = s_part + ((size_t)(gl * S * 2 + par) * 32 + lane) * 8;         // wave S gl: part 0
+          const float* p1 = s_part + ((size_t)((gl * S + 1) * 2 + par) * 32 + lane) * 8;   // wave S gl + 1: part 1
           const f32x4 g0 = *(const f32x4*)p0, u0 = *(const f32x4*)(p0 + 4);
           const f32x4 g1 = *(const f32x4*)p1, u1 = *(const f32x4*)(p1 + 4);
           f32x4 gs, us;
