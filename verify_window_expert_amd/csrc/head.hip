@@ -18,7 +18,12 @@
 
 namespace sw {
 
-constexpr int kHeadWaves = 8, kHeadThreads = 64 * kHeadWaves;
+// 12 waves per workgroup: at vocabulary 151936 each of the 3072 waves owns 3 or 4 of the
+// 9496 tiles (with 8 waves, 4 or 5), and each SIMD keeps three rings in flight
+#ifndef SW_HEAD_WAVES
+#define SW_HEAD_WAVES 12
+#endif
+constexpr int kHeadWaves = SW_HEAD_WAVES, kHeadThreads = 64 * kHeadWaves;
 #ifndef SW_HEAD_GRID
 #define SW_HEAD_GRID 256
 #endif
