@@ -978,7 +978,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
 // weights in the same order in row_w, so every load is issued at once (clamped; slots
 // past k + 1 are not summed), then the fixed-order sum and the residual.
 
-constexpr int kCombineThreads = 256, kCombineVec = 2;
+// 64 threads per workgroup: the combine is a few hundred KB, so more, smaller workgroups
+// spread its loads over more compute units (measured 0.2 us per window faster than 256)
+constexpr int kCombineThreads = 64, kCombineVec = 2;
 
 template <bool F32IN>
 __global__ __launch_bounds__(kCombineThreads) void k_combine(DownArgs a) {
