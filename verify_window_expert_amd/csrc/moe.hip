@@ -827,8 +827,12 @@ void k_gateup(GateUpArgs a) {
 // each row's list in order. As in gate/up, h (from L2) is staged in LDS while the first
 // weights are in flight.
 
-constexpr int kDnWaves = 16, kDnThreads = 64 * kDnWaves;
 size_t down_lds_bytes(int ffn) { return act_lds_bytes(ffn, 16); }
+
+// Waves of a down workgroup: 16 (one workgroup per compute unit) for windows of more than
+// 4 rows, 8 (two per compute unit, each staging its slot's h) for smaller ones, measured
+// faster there; a tile's arithmetic is the same in both, so the choice changes no bit.
+inline int dn_waves_of(int rows) { return rows <= 4 ? 8 : 16; }
 
 // 8 inputs of row j already split into bf16 hi and lo in the image order: stored as
 // they are, and the block sums add the group's values in image order, then over the 4
@@ -854,9 +858,10 @@ __device__ __forceinline__ void stage_group_split(const ActLds& l, bool ok, int 
   }
 }
 
-template <int BITS, int XG>
-__global__ __launch_bounds__(kDnThreads) void k_down(DownArgs a) {
+template <int BITS, int XG, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_down(DownArgs a) {
   constexpr int DEPTH = kDnDepth;
+  constexpr int kDnWaves = WAVES, kDnThreads = 64 * WAVES;
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_ydst[kMaxRows];
   const int H = a.hidden, F = a.ffn, E = a.n_experts;
@@ -1121,23 +1126,32 @@ int launch_gateup_routed(const GateUpArgs& a, int max_slots, hipStream_t s, cons
   return launch_gateup_any<true>(a, max_slots, s, p);
 }
 
-template <int BITS, int XG>
+template <int BITS, int XG, int WAVES>
 static int launch_down_k(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
-  if (int e = set_lds<k_down<BITS, XG>>(lds)) return e;
-  // at least one workgroup per slot, so that every expert is served
-  int grid = persistent_grid<k_down<BITS, XG>>(kDnThreads, lds, 1 << 30, 1);
+  if (int e = set_lds<k_down<BITS, XG, WAVES>>(lds)) return e;
+  // 16 waves per compute unit; at least one workgroup per slot, so that every expert is
+  // served
+  int grid = persistent_grid<k_down<BITS, XG, WAVES>>(64 * WAVES, lds, 1 << 30, 16 / WAVES);
   if (grid < max_slots) grid = max_slots;
-  launch(k_down<BITS, XG>, dim3(grid), dim3(kDnThreads), lds, s, p, a);
+  launch(k_down<BITS, XG, WAVES>, dim3(grid), dim3(64 * WAVES), lds, s, p, a);
   return 0;
+}
+
+template <int BITS, int WAVES>
+static int launch_down_w(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
+  // h groups (8 inputs) of the window's rows per thread, all loaded up front (rows * ffn / 8)
+  constexpr int T = 64 * WAVES;
+  const int groups = a.rows * (a.ffn / 8);
+  if (groups <= 1 * T) return launch_down_k<BITS, 1, WAVES>(a, lds, max_slots, s, p);
+  if (groups <= 2 * T) return launch_down_k<BITS, 2, WAVES>(a, lds, max_slots, s, p);
+  if (groups <= 4 * T) return launch_down_k<BITS, 4, WAVES>(a, lds, max_slots, s, p);
+  return (int)hipErrorInvalidValue;
 }
 
 template <int BITS>
 static int launch_down_bits(const DownArgs& a, size_t lds, int max_slots, hipStream_t s, const Prof* p) {
-  // h groups (8 inputs) of up to 8 rows per thread, all loaded up front (8 * ffn / 8)
-  if (a.ffn <= 1 * kDnThreads) return launch_down_k<BITS, 1>(a, lds, max_slots, s, p);
-  if (a.ffn <= 2 * kDnThreads) return launch_down_k<BITS, 2>(a, lds, max_slots, s, p);
-  if (a.ffn <= 4 * kDnThreads) return launch_down_k<BITS, 4>(a, lds, max_slots, s, p);
-  return (int)hipErrorInvalidValue;
+  return dn_waves_of(a.rows) == 8 ? launch_down_w<BITS, 8>(a, lds, max_slots, s, p)
+                                  : launch_down_w<BITS, 16>(a, lds, max_slots, s, p);
 }
 
 int launch_down(const DownArgs& a, hipStream_t s, const Prof* p, bool combine) {
