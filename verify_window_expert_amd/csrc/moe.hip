@@ -819,8 +819,9 @@ void k_gateup(GateUpArgs a) {
 // them; the block sums Sx the min term needs are formed while staging, in LDS.
 
 
-// k_down: persistent, 16-wave workgroups (so that each (slot, output tile) item gets a
-// wave of its own at the usual shapes); workgroup b serves expert slot b % n_active (the
+// k_down: persistent, 16 waves per compute unit (one 16-wave workgroup, or two of 8 for
+// small windows: dn_waves_of), so that each (slot, output tile) item gets a wave of its
+// own at the usual shapes; workgroup b serves expert slot b % n_active (the
 // workgroups of a slot split its output tiles) and stages that expert's h once; each
 // wave streams whole 16-row output tiles through the ring. y is written for each of the
 // expert's rows at that row's place in its ascending list of experts; k_combine sums
