@@ -172,6 +172,19 @@ def test_max_limits(layer):
     check_window(synth.config("e256_2bit", hidden=1024, ffn=256, rows=8), 0, layer=layer)
 
 
+@pytest.mark.parametrize("rows", [4, 8])
+def test_large_ffn(rows):
+    """ffn 4096: the down kernel stages the most h per thread (4 groups of 8 inputs), in
+    8-wave workgroups at 4 rows and 16-wave ones at 8; each row also equals the row alone."""
+    cfg = synth.config("two_slots_mtp", hidden=512, ffn=4096, experts=8, top_k=2, rows=rows)
+    _, gout = check_window(cfg, 0, layer=True)[:2]
+    _, dl, _ = layer_for(cfg)
+    x = synth.make_window(cfg, 0)
+    for r in range(rows):
+        _, g1, _ = gpu_window(dl, to_dev_x(x[r:r + 1]), cfg.top_k, layer=True)
+        assert np.array_equal(g1[0].view(np.uint32), gout[r].view(np.uint32)), r
+
+
 @pytest.mark.parametrize("layer", [False, True])
 def test_hidden_beyond_eight_router_chunks(layer):
     """hidden 4608: nine 512-input router chunks, more than the routing core keeps in
