@@ -27,8 +27,10 @@ constexpr int kHeadWaves = SW_HEAD_WAVES, kHeadThreads = 64 * kHeadWaves;
 #ifndef SW_HEAD_GRID
 #define SW_HEAD_GRID 256
 #endif
+// 4 units in flight per wave (48 KB per compute unit at 12 waves): measured faster than 2,
+// 3, 5, 6, 8 and 12
 #ifndef SW_HEAD_DEPTH
-#define SW_HEAD_DEPTH 8
+#define SW_HEAD_DEPTH 4
 #endif
 constexpr int kHeadGrid = SW_HEAD_GRID;     // workgroups (one per compute unit of the MI355X)
 constexpr int kHeadDepth = SW_HEAD_DEPTH;   // units (one 16-row x 64-input chunk) in flight per wave
